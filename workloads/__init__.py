@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle runs.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path and the CPU oracle are fed from here so
+that they see exactly the same bytes.
+
+Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload):
+  1. for the packed-document workload only: document lengths, integers drawn
+     uniformly from [256, 4096] one at a time until their sum reaches the total
+     length; the last one is cut so the sum is exact;
+  2. Q, then K, then V as float32 standard normals in C order, shapes
+     (B, Hq, L, D), (B, Hkv, S, D), (B, Hkv, S, D);
+  3. bfloat16 workloads round those float32 values to bfloat16 with
+     round-to-nearest-even; the widened float32 copy is then exact.
+
+The five workloads are the ones the block-sparse attention pages motivate:
+plain causal (fp32), causal with soft-cap and an ALiBi-style bias, packed
+documents, a sliding window with sink tokens under grouped-query attention,
+and a 16-query verify step against a long KV cache with the causal mask
+aligned to the bottom-right corner.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "get_workload", "draw_doc_lengths", "doc_ids_from_lengths",
+    "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits", "make_inputs",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    Inputs here are finite by construction; NaN payloads are not handled.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exactly widened float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 and return them as float32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def draw_doc_lengths(rng: np.random.Generator, total: int, lo: int = 256, hi: int = 4096) -> list:
+    """Document lengths uniform on [lo, hi], drawn until they cover ``total``; last one cut."""
+    lengths, acc = [], 0
+    while acc < total:
+        n = int(rng.integers(lo, hi + 1))
+        lengths.append(n)
+        acc += n
+    lengths[-1] -= acc - total
+    return lengths
+
+
+def doc_ids_from_lengths(lengths) -> np.ndarray:
+    """Per-position document index (int32), documents laid end to end."""
+    return np.repeat(np.arange(len(lengths), dtype=np.int32), np.asarray(lengths, dtype=np.int64))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: shapes, dtype, mask and score rule, tile shape, seed."""
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    S: int
+    D: int
+    dtype: str                  # "f32" or "bf16"
+    mask: str                   # "noop" | "causal" | "causal_window_sinks" | "doc_causal"
+    score: str                  # "none" | "softcap" | "softcap_alibi"
+    q_block: int
+    kv_block: int
+    cap: float = 0.0
+    alibi_m: float = 8.0
+    window: int = 0
+    sinks: int = 0
+    docs: bool = False          # packed documents: draw lengths first
+
+    @property
+    def q_offset(self) -> int:
+        # queries are the last L positions of the S-long sequence (bottom-right alignment)
+        return self.S - self.L
+
+
+WORKLOADS = {
+    "causal_f32": Workload("causal_f32", 1, 1, 2, 2, 256, 256, 64, "f32", "causal", "none", 64, 64),
+    "causal_softcap_alibi": Workload("causal_softcap_alibi", 2, 4, 16, 16, 2048, 2048, 64, "bf16",
+                                     "causal", "softcap_alibi", 128, 64, cap=30.0, alibi_m=8.0),
+    "doc_causal": Workload("doc_causal", 3, 1, 16, 16, 16384, 16384, 128, "bf16", "doc_causal", "none",
+                           128, 64, docs=True),
+    "window_sinks_gqa": Workload("window_sinks_gqa", 4, 2, 32, 8, 8192, 8192, 128, "bf16",
+                                 "causal_window_sinks", "softcap", 128, 64, cap=50.0, window=1024, sinks=4),
+    "decode_verify": Workload("decode_verify", 5, 16, 32, 8, 16, 32768, 128, "bf16", "causal", "softcap",
+                              16, 64, cap=50.0),
+}
+WORKLOAD_ORDER = ["causal_f32", "causal_softcap_alibi", "doc_causal", "window_sinks_gqa", "decode_verify"]
+
+
+def get_workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def make_inputs(w: Workload, *, B: Optional[int] = None, seed: Optional[int] = None) -> dict:
+    """Draw the workload's inputs.
+
+    Returns a dict with ``q``, ``k``, ``v`` as float32 arrays (for bf16 workloads these
+    are the exactly widened bf16 values), ``q_bits``/``k_bits``/``v_bits`` as uint16 for
+    bf16 workloads, ``doc_id`` (int32, or None) and ``doc_lengths``.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    B = w.B if B is None else B
+    doc_lengths, doc_id = None, None
+    if w.docs:
+        doc_lengths = draw_doc_lengths(rng, w.S)
+        doc_id = doc_ids_from_lengths(doc_lengths)
+    out = {"doc_lengths": doc_lengths, "doc_id": doc_id}
+    for name, shape in (("q", (B, w.Hq, w.L, w.D)), ("k", (B, w.Hkv, w.S, w.D)), ("v", (B, w.Hkv, w.S, w.D))):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if w.dtype == "bf16":
+            bits = f32_to_bf16_bits(x)
+            del x
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_f32(bits)
+        else:
+            out[name] = x
+    return out
