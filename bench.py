@@ -1,0 +1,211 @@
+"""Benchmark of the block-sparse attention forward hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of seeded synthetic input
+already resident in HBM: the BlockMask build from the mask_mod, then the fused
+forward (QK^T, scale, score_mod, partial-tile mask, online softmax, PV, out and
+lse).  The default workload is causal attention with a soft-cap plus ALiBi-
+slope score_mod at B=4, H=16, L=S=2048, D=64, bf16, 128x64 tiles.
+
+Throughput is counted over visited-block FLOPs: 4*D per cell of every full or
+partial tile (clipped to the sequence bounds), times B*Hq.  The roofline entry
+times the forward kernel alone with HIP events on the stream it runs on.  The
+CPU baseline times the float64 oracle on a bounded sample of the same workload
+and checks the GPU output on those rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 matrix
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="causal_softcap_alibi")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
+    return p.parse_args()
+
+
+def visited_flops_per_head(bm_np, w):
+    """4*D * cells of every listed tile (clipped to L, S), per (batch, head) of mask row (0, 0)."""
+    total = 0
+    nqb = bm_np["kv_num_blocks"].shape[2]
+    for qb in range(nqb):
+        rows = min(w.q_block, w.L - qb * w.q_block)
+        for num, idx in (("kv_num_blocks", "kv_indices"), ("full_kv_num_blocks", "full_kv_indices")):
+            n = int(bm_np[num][0, 0, qb])
+            for kb in bm_np[idx][0, 0, qb, :n]:
+                total += rows * min(w.kv_block, w.S - int(kb) * w.kv_block)
+    return 4 * w.D * total
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print("bench.py: multi-GPU runs are not part of this build (one GPU per box); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import programmable_block_sparse_amd as pbs
+    from workloads import WORKLOADS, make_inputs
+    from workloads.torch_io import specs, to_device
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    q, k, v, doc_t = to_device(w, inp, dev)
+    mspec, sspec = specs(w, doc_t)
+    print(f"bench: workload {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} L={w.L} S={w.S} D={w.D} {w.dtype} "
+          f"mask={w.mask} score={w.score} tiles {w.q_block}x{w.kv_block}", file=sys.stderr, flush=True)
+
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    torch.cuda.synchronize()
+    bm_np = {n: getattr(bm, n).cpu().numpy() for n in
+             ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices")}
+    flops = visited_flops_per_head(bm_np, w) * w.B * w.Hq
+    elem = 2 if w.dtype == "bf16" else 4
+    alg_bytes = (w.B * w.Hq * w.L * w.D + 2 * w.B * w.Hkv * w.S * w.D + w.B * w.Hq * w.L * w.D) * elem \
+        + w.B * w.Hq * w.L * 4
+    out = torch.empty((w.B, w.Hq, w.L, w.D), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device=dev)
+    ws_bytes = pbs.flex_attn_fwd_workspace_bytes(q.dtype, w.B, w.Hq, w.Hkv, w.L, w.S, w.D, bm)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
+
+    def step():
+        b2 = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+        pbs.flex_attn_fwd(q, k, v, block_mask=b2, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
+
+    def build_only():
+        pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    ms_step = timed(step, args.steps)
+    ms_fwd = timed(fwd, args.steps)
+    ms_mask = timed(build_only, args.steps)
+    print(f"bench: step {ms_step * 1e3:.1f} us, fwd {ms_fwd * 1e3:.1f} us, block mask {ms_mask * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
+    if w.name == "decode_verify":
+        roof = {"bound": "hbm", "achieved": alg_bytes / (ms_fwd * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "attn_fwd_prefill"
+    roof["algorithmic_per_launch"] = flops if roof["unit"] == "TFLOP/s" else alg_bytes
+
+    result = {
+        "metric": "flex fwd TFLOP/s (visited-block FLOPs) and % of MI355X bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, PCG64 seed %d)" % w.seed,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "D": w.D,
+                   "mask": w.mask, "score": w.score, "cap": w.cap, "window": w.window, "sinks": w.sinks,
+                   "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset,
+                   "doc_lengths": inp["doc_lengths"]},
+        "roofline": roof,
+        "fwd_ms": ms_fwd, "blockmask_ms": ms_mask,
+        "fwd_tflops_visited": fwd_tflops, "pct_bf16_peak_fwd": 100.0 * fwd_tflops / BF16_PEAK_TFLOPS,
+        "visited_block_flops": flops, "algorithmic_bytes": alg_bytes,
+        "hbm_gbs_fwd": alg_bytes / (ms_fwd * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        result.update(cpu_baseline(args, w, inp, out, lse, flops))
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, w, inp, out, lse, flops):
+    """Time the float64 oracle on whole (batch, head) slices of the workload and
+    compare the GPU output on those rows."""
+    import torch
+    from oracle import MaskMod, ScoreMod, attention, build_block_mask
+    import programmable_block_sparse_amd as pbs
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"])
+    smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
+    t0 = time.perf_counter()
+    ref_bm = build_block_mask(mmod, w.L, w.S, w.q_block, w.kv_block, q_offset=w.q_offset)
+    visible = int(ref_bm["counts"].sum())
+    t_bm = time.perf_counter() - t0
+    heads_total = w.B * w.Hq
+    per_head_flops = flops / heads_total
+    # about 10 s of work: calibrate on one head, then run the rest of the sample
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    t0 = time.perf_counter()
+    o1, l1 = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod, mask=mmod,
+                       q_offset=w.q_offset, heads=[0], batches=[0])
+    t_one = time.perf_counter() - t0
+    n = args.cpu_sample_heads or int(max(1, min(len(pairs), 10.0 // max(t_one, 1e-3))))
+    sample = pairs[:n]
+    outs = {(0, 0): (o1, l1)}
+    t0 = time.perf_counter()
+    for (b, h) in sample[1:]:
+        outs[(b, h)] = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod,
+                                 mask=mmod, q_offset=w.q_offset, heads=[h], batches=[b])
+    t_rest = time.perf_counter() - t0
+    t_total = t_one + t_rest
+    out_np = out.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    err_o = max(float(np.abs(out_np[b, h] - outs[(b, h)][0][0, 0]).max()) for (b, h) in sample)
+    fin = [np.isfinite(outs[(b, h)][1][0, 0]) for (b, h) in sample]
+    err_l = max(float(np.abs(lse_np[b, h][f] - outs[(b, h)][1][0, 0][f]).max()) if f.any() else 0.0
+                for (b, h), f in zip(sample, fin))
+    return {
+        "cpu_baseline": {"value": per_head_flops * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
+                         "cores": blas_threads or cores, "kind": "oracle",
+                         "sample": f"{len(sample)} of {heads_total} (batch, head) slices, all {w.L} rows each; "
+                                   f"float64 dense oracle, {t_total:.1f} s; host cores {cores}"},
+        "cpu_blockmask_oracle_s": t_bm,
+        "visible_element_flops": 4 * w.D * visible * w.B * w.Hq,
+        "parity_on_bench_buffers": {"out_max_abs": err_o, "lse_max_abs": err_l, "rows_checked": len(sample) * w.L},
+    }
+
+
+if __name__ == "__main__":
+    main()

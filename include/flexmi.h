@@ -1,0 +1,204 @@
+/*
+ * flexmi.h -- C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * The library computes the forward pass of programmable block-sparse attention
+ * (the FlexAttention formulation):
+ *
+ *   s_ij  = scale * q_i . k_j
+ *   z_ij  = g(s_ij, b, h, p_i, j)   if M(b, h, p_i, j)        else -inf
+ *   o_i   = sum_j softmax_j(z_ij) v_j,   lse_i = log sum_j exp(z_ij)
+ *
+ * where g is a score_mod, M a mask_mod (true = attend) and p_i = i + q_offset
+ * the logical position of query row i.  Source: charlestar blog "FlexAttention
+ * score_mod / BlockMask", section on what one connection goes through (the
+ * formula and the order: scaled score, then g, then visibility, then the
+ * normalised sum of values) and its decode section (logical query position).
+ * The call shape follows the 2kiu "PyTorch Flex Attention complete guide",
+ * section 1.1 (query (B,Hq,L,E), key (B,Hkv,S,E), value (B,Hkv,S,Ev), scale,
+ * GQA, output (B,Hq,L,Ev)) and section 2 (lse of shape (B,Hq,L)).
+ *
+ * score_mod and mask_mod are not arbitrary programs here: they are chosen from
+ * a fixed menu (the enums below) with run-time parameters.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must be HIP device memory (or memory
+ *     the device can access); parameter structs are host memory read during
+ *     the call only.  The caller owns every buffer.  The library keeps no
+ *     state between calls, never allocates and never synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   - All argument checks run on the host before any HIP call, so an invalid
+ *     call returns an error code and enqueues nothing.  A failing kernel
+ *     launch returns FLEX_ERR_HIP.  flex_last_error() gives a one-line reason
+ *     for the last failure on the calling thread.
+ *   - Sizes are element counts; strides are element strides.
+ */
+#ifndef FLEXMI_H
+#define FLEXMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FLEX_OK = 0,
+    FLEX_ERR_NULL = 1,         /* a required pointer is NULL */
+    FLEX_ERR_SHAPE = 2,        /* non-positive or out-of-range size */
+    FLEX_ERR_GQA = 3,          /* Hq is not a multiple of Hkv */
+    FLEX_ERR_BLOCKMASK = 4,    /* block mask dims do not match L, S, B, Hq */
+    FLEX_ERR_UNSUPPORTED = 5,  /* dtype, head dim, tile shape or menu entry not provided */
+    FLEX_ERR_LAYOUT = 6,       /* pointer or stride not 16-byte aligned */
+    FLEX_ERR_WORKSPACE = 7,    /* workspace missing or smaller than required */
+    FLEX_ERR_HIP = 8,          /* a HIP call or kernel launch failed */
+    FLEX_ERR_PARAM = 9         /* invalid mask or score parameter */
+} flex_status;
+
+typedef enum { FLEX_F32 = 0, FLEX_BF16 = 1 } flex_dtype;
+
+/* mask_mod menu.  Each returns true when query position p may attend key j.
+ *   NOOP                 always true (2kiu guide, section 4.4)
+ *   CAUSAL               j <= p (quant67 "Causal Mask" article; with
+ *                        q_offset = S - L this is the bottom-right alignment of
+ *                        its section 4)
+ *   CAUSAL_WINDOW_SINKS  j <= p and (p - j < window or j < sinks): a causal
+ *                        window of `window` keys counting the query itself
+ *                        (charlestar blog, pinned-version example) plus the
+ *                        first `sinks` keys (tensorcad "Attention expressions",
+ *                        Examples, sink window)
+ *   DOC_CAUSAL           j <= p and doc_id[p] == doc_id[j] (charlestar blog,
+ *                        packing section; quant67 article section 7 demo) */
+typedef enum {
+    FLEX_MASK_NOOP = 0,
+    FLEX_MASK_CAUSAL = 1,
+    FLEX_MASK_CAUSAL_WINDOW_SINKS = 2,
+    FLEX_MASK_DOC_CAUSAL = 3
+} flex_mask_kind;
+
+/* score_mod menu, applied to the already scaled score s of every computed cell
+ * (full and partial tiles alike) before the mask.
+ *   NONE            g = s
+ *   SOFTCAP         g = cap * tanh(s / cap)   (tensorcad Examples, Gemma-2 cap)
+ *   SOFTCAP_ALIBI   g = cap * tanh(s / cap) + alpha_h * (j - p),
+ *                   alpha_h = 2^(-alibi_m * (h + 1) / Hq), h the query head
+ *                   (charlestar blog, score_mod ordering section: cap first,
+ *                   bias after; tensorcad Examples, ALiBi slope) */
+typedef enum {
+    FLEX_SCORE_NONE = 0,
+    FLEX_SCORE_SOFTCAP = 1,
+    FLEX_SCORE_SOFTCAP_ALIBI = 2
+} flex_score_kind;
+
+/* Mask parameters (host struct).
+ *   kind      a flex_mask_kind
+ *   window    CAUSAL_WINDOW_SINKS: window length, >= 1
+ *   sinks     CAUSAL_WINDOW_SINKS: number of always-visible leading keys, >= 0
+ *   q_offset  logical position of query row 0 (S - L aligns the causal
+ *             diagonal bottom-right; 0 aligns it top-left)
+ *   doc_id    DOC_CAUSAL: device int32[doc_len], document index per position
+ *   doc_len   DOC_CAUSAL: must cover every key and query position, i.e.
+ *             doc_len >= max(S, q_offset + L) with q_offset >= 0 */
+typedef struct {
+    int32_t kind;
+    int32_t window;
+    int32_t sinks;
+    int32_t reserved;
+    int64_t q_offset;
+    const int32_t* doc_id;
+    int64_t doc_len;
+} flex_mask_params;
+
+/* Score parameters (host struct).  cap > 0 for the SOFTCAP kinds. */
+typedef struct {
+    int32_t kind;
+    float cap;
+    float alibi_m;
+} flex_score_params;
+
+/* BlockMask (2kiu guide, sections 3.1-3.2 and 4.1).  Tiles are
+ * q_block x kv_block cells; num_q_blocks = ceil(L / q_block),
+ * num_kv_blocks = ceil(S / kv_block).  B and H are 1 (the mask is the same for
+ * every batch / head and is broadcast) or the full batch / query-head count.
+ * Device arrays, int32, C order:
+ *   kv_num_blocks       [B][H][num_q_blocks]   number of partial tiles per row
+ *   kv_indices          [B][H][num_q_blocks][num_kv_blocks]
+ *                       the partial tiles' kv-block indices ascending, then the
+ *                       remaining indices ascending
+ *   full_kv_num_blocks  same shape as kv_num_blocks, full tiles
+ *   full_kv_indices     same layout as kv_indices, full tiles
+ * A tile is full when every one of its cells is visible, empty when none is
+ * and partial otherwise; cells beyond L or S count as not visible. */
+typedef struct {
+    int32_t B, H;
+    int32_t q_block, kv_block;
+    int32_t num_q_blocks, num_kv_blocks;
+    int32_t* kv_num_blocks;
+    int32_t* kv_indices;
+    int32_t* full_kv_num_blocks;
+    int32_t* full_kv_indices;
+} flex_block_mask;
+
+/* Build a BlockMask from a mask_mod by evaluating it on every cell of every
+ * tile (2kiu guide, section 4.1, create_block_mask with separate full blocks;
+ * charlestar blog, BlockMask section, for the three tile classes).  No dense
+ * element mask is ever formed.
+ *   mask  mask parameters (q_offset, doc_id as for flex_attn_fwd)
+ *   L, S  query and key lengths, 1 <= L, S < 2^30
+ *   bm    dims filled in by the caller (B, H in {1, ...}, 1 <= q_block,
+ *         kv_block <= 1024, num_q_blocks, num_kv_blocks as above) and the four
+ *         caller-allocated device arrays, all written by this call
+ * Errors: NULL, SHAPE, BLOCKMASK (dims), PARAM (mask parameters), HIP. */
+flex_status flex_blockmask_build(const flex_mask_params* mask, int64_t L, int64_t S,
+                                 const flex_block_mask* bm, void* stream);
+
+/* Bytes of device workspace flex_attn_fwd needs for these sizes (0 when the
+ * call needs none).  Returns 0 for arguments flex_attn_fwd would reject. */
+size_t flex_attn_fwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int64_t L, int64_t S, int32_t D,
+                                     const flex_block_mask* bm);
+
+/* Block-sparse attention forward.
+ *   q, k, v      device tensors of `dtype` (FLEX_F32 or FLEX_BF16) with shapes
+ *                q (B,Hq,L,D), k and v (B,Hkv,S,D); the last dimension is
+ *                contiguous, the other three use the given element strides
+ *                (q_strides = {batch, head, row}); base pointers and strides
+ *                must be 16-byte aligned
+ *   D            head dimension, 64 or 128
+ *   Hq % Hkv     must be 0; query head h reads K/V head h / (Hq / Hkv)
+ *   scale        multiplier of q.k; scale <= 0 selects 1/sqrt(D) (2kiu guide,
+ *                section 6.2), computed in fp32
+ *   score, mask  menu entries and their parameters
+ *   bm           BlockMask built for the same mask parameters and (L, S);
+ *                q_block in {16, 32, 64, 128}, kv_block a multiple of 64.
+ *                It must be rebuilt whenever q_offset or doc_id changes
+ *                (charlestar blog, decode and cache sections): the library
+ *                trusts the lists and cannot detect a stale mask.
+ *   out          device, (B,Hq,L,D) contiguous, dtype `dtype` (bf16 is
+ *                rounded to nearest even)
+ *   lse          device float32 (B,Hq,L) contiguous, or NULL when not wanted
+ *   workspace    device scratch of at least flex_attn_fwd_workspace_bytes()
+ *                (may be NULL when that is 0)
+ * Rows with no visible key get out = 0 and lse = -inf.
+ * Errors: NULL, SHAPE, GQA, BLOCKMASK, UNSUPPORTED, LAYOUT, WORKSPACE, PARAM,
+ * HIP. */
+flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t dtype,
+                          int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D,
+                          const int64_t q_strides[3], const int64_t k_strides[3],
+                          const int64_t v_strides[3], float scale,
+                          const flex_score_params* score, const flex_mask_params* mask,
+                          const flex_block_mask* bm, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static name of a status code. */
+const char* flex_status_string(int32_t status);
+
+/* Reason for the failure of the calling thread's last library call ("" if it
+ * succeeded).  The pointer stays valid until the thread's next library call. */
+const char* flex_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXMI_H */

@@ -1,0 +1,255 @@
+"""Python binding of libflexmi (MI355X block-sparse attention forward).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI in ``include/flexmi.h``.  torch supplies device
+memory and the current stream.  The binding exposes the C entry points under
+the same names:
+
+  flex_blockmask_build(mask, L, S, q_block, kv_block, ...) -> BlockMask
+  flex_attn_fwd(q, k, v, score=..., mask=..., block_mask=..., ...) -> (out, lse)
+  flex_attn_fwd_workspace_bytes(...)
+  flex_status_string(code)
+
+There is no fallback: if the native library is missing or cannot load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch  # imported first so the library binds to torch's HIP runtime
+
+__all__ = [
+    "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
+    "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_workspace_bytes", "flex_status_string",
+    "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+MASK_KINDS = {"noop": 0, "causal": 1, "causal_window_sinks": 2, "doc_causal": 3}
+SCORE_KINDS = {"none": 0, "softcap": 1, "softcap_alibi": 2}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd",
+                    "flex_status_string", "flex_last_error")
+
+
+class flex_mask_params(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32), ("sinks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("doc_id", ctypes.c_void_p),
+                ("doc_len", ctypes.c_int64)]
+
+
+class flex_score_params(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("cap", ctypes.c_float), ("alibi_m", ctypes.c_float)]
+
+
+class flex_block_mask(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("q_block", ctypes.c_int32),
+                ("kv_block", ctypes.c_int32), ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
+                ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("FLEXMI_LIBRARY", os.path.join(_HERE, "libflexmi.so"))
+
+
+def load_library():
+    """Load libflexmi.so (built by ``programmable_block_sparse_amd.build``); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"native library {path} is missing: run programmable_block_sparse_amd.build first")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    I64x3 = ctypes.POINTER(ctypes.c_int64)
+    lib.flex_blockmask_build.argtypes = [ctypes.POINTER(flex_mask_params), I64, I64,
+                                         ctypes.POINTER(flex_block_mask), P]
+    lib.flex_blockmask_build.restype = ctypes.c_int
+    lib.flex_attn_fwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I64, I64, I32, ctypes.POINTER(flex_block_mask)]
+    lib.flex_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.flex_attn_fwd.argtypes = [P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3, ctypes.c_float,
+                                  ctypes.POINTER(flex_score_params), ctypes.POINTER(flex_mask_params),
+                                  ctypes.POINTER(flex_block_mask), P, P, P, ctypes.c_size_t, P]
+    lib.flex_attn_fwd.restype = ctypes.c_int
+    lib.flex_status_string.argtypes = [I32]
+    lib.flex_status_string.restype = ctypes.c_char_p
+    lib.flex_last_error.argtypes = []
+    lib.flex_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+class FlexError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{flex_status_string(status)}: {detail}")
+
+
+def flex_status_string(status: int) -> str:
+    return load_library().flex_status_string(int(status)).decode()
+
+
+def flex_last_error() -> str:
+    return load_library().flex_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise FlexError(status, flex_last_error())
+
+
+@dataclasses.dataclass
+class MaskSpec:
+    """mask_mod menu entry.  ``q_offset=None`` means bottom-right alignment (S - L)."""
+    kind: str = "noop"
+    window: int = 0
+    sinks: int = 0
+    q_offset: Optional[int] = None
+    doc_id: Optional[torch.Tensor] = None   # int32 device tensor for "doc_causal"
+
+    def to_c(self, L: int, S: int) -> flex_mask_params:
+        m = flex_mask_params()
+        m.kind = MASK_KINDS[self.kind]
+        m.window = int(self.window)
+        m.sinks = int(self.sinks)
+        m.q_offset = int(S - L if self.q_offset is None else self.q_offset)
+        if self.doc_id is not None:
+            if self.doc_id.dtype != torch.int32 or not self.doc_id.is_contiguous():
+                raise ValueError("doc_id must be a contiguous int32 tensor")
+            m.doc_id = self.doc_id.data_ptr()
+            m.doc_len = self.doc_id.numel()
+        return m
+
+
+@dataclasses.dataclass
+class ScoreSpec:
+    """score_mod menu entry."""
+    kind: str = "none"
+    cap: float = 0.0
+    alibi_m: float = 8.0
+
+    def to_c(self) -> flex_score_params:
+        s = flex_score_params()
+        s.kind = SCORE_KINDS[self.kind]
+        s.cap = float(self.cap)
+        s.alibi_m = float(self.alibi_m)
+        return s
+
+
+@dataclasses.dataclass
+class BlockMask:
+    """The four BlockMask arrays (int32 device tensors) and their dims."""
+    kv_num_blocks: torch.Tensor
+    kv_indices: torch.Tensor
+    full_kv_num_blocks: torch.Tensor
+    full_kv_indices: torch.Tensor
+    q_block: int
+    kv_block: int
+    L: int
+    S: int
+
+    @property
+    def B(self) -> int:
+        return self.kv_num_blocks.shape[0]
+
+    @property
+    def H(self) -> int:
+        return self.kv_num_blocks.shape[1]
+
+    def to_c(self) -> flex_block_mask:
+        c = flex_block_mask()
+        c.B, c.H = self.B, self.H
+        c.q_block, c.kv_block = self.q_block, self.kv_block
+        c.num_q_blocks, c.num_kv_blocks = self.kv_indices.shape[2], self.kv_indices.shape[3]
+        c.kv_num_blocks = self.kv_num_blocks.data_ptr()
+        c.kv_indices = self.kv_indices.data_ptr()
+        c.full_kv_num_blocks = self.full_kv_num_blocks.data_ptr()
+        c.full_kv_indices = self.full_kv_indices.data_ptr()
+        return c
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def flex_blockmask_build(mask: MaskSpec, L: int, S: int, q_block: int, kv_block: int, *, B: int = 1, H: int = 1,
+                         device="cuda") -> BlockMask:
+    """Allocate the BlockMask tensors and fill them on the GPU (C: flex_blockmask_build)."""
+    lib = load_library()
+    nqb, nkb = -(-L // q_block), -(-S // kv_block)
+    dev = torch.device(device)
+    t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    bm = BlockMask(t(B, H, nqb), t(B, H, nqb, nkb), t(B, H, nqb), t(B, H, nqb, nkb), q_block, kv_block, L, S)
+    cm = mask.to_c(L, S)
+    cbm = bm.to_c()
+    _check(lib.flex_blockmask_build(ctypes.byref(cm), L, S, ctypes.byref(cbm), ctypes.c_void_p(_stream_ptr(dev))))
+    return bm
+
+
+def flex_attn_fwd_workspace_bytes(dtype: torch.dtype, B: int, Hq: int, Hkv: int, L: int, S: int, D: int,
+                                  block_mask: BlockMask) -> int:
+    lib = load_library()
+    cbm = block_mask.to_c()
+    return int(lib.flex_attn_fwd_workspace_bytes(DTYPES[dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
+
+
+def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_mask: BlockMask,
+                  score: Optional[ScoreSpec] = None, mask: Optional[MaskSpec] = None,
+                  scale: Optional[float] = None, return_lse: bool = True,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Block-sparse attention forward (C: flex_attn_fwd).
+
+    q (B, Hq, L, D), k and v (B, Hkv, S, D) device tensors of one dtype (float32 or
+    bfloat16) with a contiguous last dim.  Returns (out, lse); lse is None when
+    ``return_lse`` is false.  ``scale=None`` selects 1/sqrt(D).
+    """
+    lib = load_library()
+    score = score or ScoreSpec()
+    mask = mask or MaskSpec()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k and v must be 4-D (B, H, seq, D)")
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D or v.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPES:
+        raise ValueError("q, k, v must share a dtype, float32 or bfloat16")
+    for t in (q, k, v):
+        if t.stride(3) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    cbm = block_mask.to_c()
+    ws_bytes = int(lib.flex_attn_fwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    cs, cm = score.to_c(), mask.to_c(L, S)
+    status = lib.flex_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
+        ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs), ctypes.byref(cm),
+        ctypes.byref(cbm), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        None if not ws_bytes else workspace.data_ptr(), ws_bytes, ctypes.c_void_p(_stream_ptr(q.device)))
+    _check(status)
+    return out, lse
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) rounded to float32, the value the library uses for scale <= 0."""
+    import numpy as np
+    return float(np.float32(1.0) / np.sqrt(np.float32(D)))

@@ -1,0 +1,253 @@
+// C ABI of the library (declared in include/flexmi.h): argument checks on the
+// host, then dispatch to the kernel launchers.  No entry point allocates,
+// synchronises or keeps state; every check runs before the first HIP call.
+//
+// The checks restate the 2kiu "PyTorch Flex Attention complete guide",
+// section 1.3 (4-D inputs, Hq == Hkv unless grouped, Hq % Hkv == 0, block mask
+// sized to the query and key lengths: "too small / too large"), plus the
+// limits of this implementation (head dims, tile shapes, alignment).
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+#include <string>
+
+#include "flexmi.h"
+#include "internal.hpp"
+
+using namespace flexmi;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+flex_status fail(flex_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions and offsets fit in int32
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
+    if (m->kind < FLEX_MASK_NOOP || m->kind > FLEX_MASK_DOC_CAUSAL)
+        return fail(FLEX_ERR_PARAM, "unknown mask kind %d", m->kind);
+    if (m->q_offset <= -kMaxLen || m->q_offset >= kMaxLen || m->q_offset + L >= kMaxLen)
+        return fail(FLEX_ERR_PARAM, "q_offset %lld out of range for L=%lld", (long long)m->q_offset, (long long)L);
+    if (m->kind == FLEX_MASK_CAUSAL_WINDOW_SINKS) {
+        if (m->window < 1) return fail(FLEX_ERR_PARAM, "window must be >= 1 (got %d)", m->window);
+        if (m->sinks < 0) return fail(FLEX_ERR_PARAM, "sinks must be >= 0 (got %d)", m->sinks);
+    }
+    if (m->kind == FLEX_MASK_DOC_CAUSAL) {
+        if (m->doc_id == nullptr) return fail(FLEX_ERR_NULL, "DOC_CAUSAL needs doc_id");
+        if (m->q_offset < 0) return fail(FLEX_ERR_PARAM, "DOC_CAUSAL needs q_offset >= 0");
+        const int64_t need = std::max<int64_t>(S, m->q_offset + L);
+        if (m->doc_len < need || m->doc_len >= kMaxLen)
+            return fail(FLEX_ERR_PARAM, "doc_len %lld must cover max(S, q_offset + L) = %lld",
+                        (long long)m->doc_len, (long long)need);
+        if (reinterpret_cast<uintptr_t>(m->doc_id) & 3u)
+            return fail(FLEX_ERR_LAYOUT, "doc_id must be 4-byte aligned");
+    }
+    return FLEX_OK;
+}
+
+MaskArgs to_mask_args(const flex_mask_params* m) {
+    MaskArgs a;
+    a.kind = m->kind;
+    a.window = m->window;
+    a.sinks = m->sinks;
+    a.q_offset = (int)m->q_offset;
+    a.doc_id = m->doc_id;
+    a.doc_len = (int)std::min<int64_t>(m->doc_len, kMaxLen - 1);
+    return a;
+}
+
+flex_status check_bm_arrays(const flex_block_mask* bm) {
+    if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
+        return fail(FLEX_ERR_NULL, "block mask arrays must not be NULL");
+    return FLEX_OK;
+}
+
+flex_status check_bm_dims(const flex_block_mask* bm, int64_t L, int64_t S) {
+    if (bm->q_block < 1 || bm->kv_block < 1 || bm->q_block > 1024 || bm->kv_block > 1024)
+        return fail(FLEX_ERR_BLOCKMASK, "block sizes must be in [1, 1024] (got %d x %d)", bm->q_block, bm->kv_block);
+    const int64_t nqb = ceil_div(L, bm->q_block), nkb = ceil_div(S, bm->kv_block);
+    if (bm->num_q_blocks != nqb)
+        return fail(FLEX_ERR_BLOCKMASK, "block mask has %d Q blocks, L=%lld needs %lld (mask too %s)",
+                    bm->num_q_blocks, (long long)L, (long long)nqb, bm->num_q_blocks < nqb ? "small" : "large");
+    if (bm->num_kv_blocks != nkb)
+        return fail(FLEX_ERR_BLOCKMASK, "block mask has %d KV blocks, S=%lld needs %lld (mask too %s)",
+                    bm->num_kv_blocks, (long long)S, (long long)nkb, bm->num_kv_blocks < nkb ? "small" : "large");
+    if (bm->B < 1 || bm->H < 1 || bm->B > 65535 || bm->H > 65535)
+        return fail(FLEX_ERR_BLOCKMASK, "block mask B=%d H=%d out of range", bm->B, bm->H);
+    return FLEX_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* flex_status_string(int32_t s) {
+    switch (s) {
+    case FLEX_OK: return "FLEX_OK";
+    case FLEX_ERR_NULL: return "FLEX_ERR_NULL";
+    case FLEX_ERR_SHAPE: return "FLEX_ERR_SHAPE";
+    case FLEX_ERR_GQA: return "FLEX_ERR_GQA";
+    case FLEX_ERR_BLOCKMASK: return "FLEX_ERR_BLOCKMASK";
+    case FLEX_ERR_UNSUPPORTED: return "FLEX_ERR_UNSUPPORTED";
+    case FLEX_ERR_LAYOUT: return "FLEX_ERR_LAYOUT";
+    case FLEX_ERR_WORKSPACE: return "FLEX_ERR_WORKSPACE";
+    case FLEX_ERR_HIP: return "FLEX_ERR_HIP";
+    case FLEX_ERR_PARAM: return "FLEX_ERR_PARAM";
+    default: return "FLEX_ERR_UNKNOWN";
+    }
+}
+
+const char* flex_last_error(void) { return g_last_error.c_str(); }
+
+flex_status flex_blockmask_build(const flex_mask_params* mask, int64_t L, int64_t S, const flex_block_mask* bm,
+                                 void* stream) {
+    g_last_error.clear();
+    if (!mask || !bm) return fail(FLEX_ERR_NULL, "mask and bm must not be NULL");
+    if (flex_status s = check_bm_arrays(bm)) return s;
+    if (L < 1 || S < 1 || L >= kMaxLen || S >= kMaxLen)
+        return fail(FLEX_ERR_SHAPE, "L=%lld S=%lld must be in [1, 2^30)", (long long)L, (long long)S);
+    if (flex_status s = check_bm_dims(bm, L, S)) return s;
+    if (bm->num_kv_blocks > 65536)
+        return fail(FLEX_ERR_UNSUPPORTED, "at most 65536 KV blocks per row (got %d)", bm->num_kv_blocks);
+    if (flex_status s = check_mask(mask, L, S)) return s;
+
+    BuildArgs a;
+    a.mask = to_mask_args(mask);
+    a.L = (int)L;
+    a.S = (int)S;
+    a.q_block = bm->q_block;
+    a.kv_block = bm->kv_block;
+    a.nQB = bm->num_q_blocks;
+    a.nKB = bm->num_kv_blocks;
+    a.Bm = bm->B;
+    a.Hm = bm->H;
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    (void)hipGetLastError();
+    hipError_t e = launch_blockmask_build(a, as_stream(stream));
+    if (e != hipSuccess) return fail(FLEX_ERR_HIP, "block mask build launch failed: %s", hipGetErrorString(e));
+    return FLEX_OK;
+}
+
+static flex_status check_fwd(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                             int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t* qs, const int64_t* ks,
+                             const int64_t* vs, const flex_score_params* score, const flex_mask_params* mask,
+                             const flex_block_mask* bm, const void* out, const float* lse) {
+    if (!q || !k || !v || !out) return fail(FLEX_ERR_NULL, "q, k, v and out must not be NULL");
+    if (!qs || !ks || !vs) return fail(FLEX_ERR_NULL, "stride arrays must not be NULL");
+    if (!score || !mask || !bm) return fail(FLEX_ERR_NULL, "score, mask and bm must not be NULL");
+    if (flex_status s = check_bm_arrays(bm)) return s;
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || L >= kMaxLen || S >= kMaxLen)
+        return fail(FLEX_ERR_SHAPE, "sizes must be positive and L, S < 2^30 (B=%d Hq=%d Hkv=%d L=%lld S=%lld)", B,
+                    Hq, Hkv, (long long)L, (long long)S);
+    if (Hq % Hkv != 0) return fail(FLEX_ERR_GQA, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (dtype != FLEX_F32 && dtype != FLEX_BF16) return fail(FLEX_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (D != 64 && D != 128) return fail(FLEX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if (flex_status s = check_bm_dims(bm, L, S)) return s;
+    if (bm->B != 1 && bm->B != B) return fail(FLEX_ERR_BLOCKMASK, "block mask B=%d must be 1 or %d", bm->B, B);
+    if (bm->H != 1 && bm->H != Hq) return fail(FLEX_ERR_BLOCKMASK, "block mask H=%d must be 1 or Hq=%d", bm->H, Hq);
+    if (bm->q_block != 16 && bm->q_block != 32 && bm->q_block != 64 && bm->q_block != 128)
+        return fail(FLEX_ERR_UNSUPPORTED, "q_block %d not supported (16, 32, 64, 128)", bm->q_block);
+    if (bm->kv_block % 64 != 0) return fail(FLEX_ERR_UNSUPPORTED, "kv_block %d must be a multiple of 64", bm->kv_block);
+    if ((int64_t)bm->num_q_blocks * B * Hq >= 2147483647LL)
+        return fail(FLEX_ERR_SHAPE, "too many (Q block, head, batch) work items");
+    const int64_t chunk = dtype == FLEX_BF16 ? 8 : 4;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(FLEX_ERR_LAYOUT, "q, k, v and out must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FLEX_ERR_LAYOUT, "lse must be 4-byte aligned");
+    for (int i = 0; i < 3; ++i)
+        if (qs[i] % chunk || ks[i] % chunk || vs[i] % chunk || qs[i] < 0 || ks[i] < 0 || vs[i] < 0)
+            return fail(FLEX_ERR_LAYOUT, "strides must be non-negative multiples of %lld elements", (long long)chunk);
+    if (score->kind < FLEX_SCORE_NONE || score->kind > FLEX_SCORE_SOFTCAP_ALIBI)
+        return fail(FLEX_ERR_PARAM, "unknown score kind %d", score->kind);
+    if (score->kind != FLEX_SCORE_NONE && !(score->cap > 0.0f && std::isfinite(score->cap)))
+        return fail(FLEX_ERR_PARAM, "soft-cap needs a finite cap > 0");
+    if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI && !std::isfinite(score->alibi_m))
+        return fail(FLEX_ERR_PARAM, "alibi_m must be finite");
+    return check_mask(mask, L, S);
+}
+
+size_t flex_attn_fwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
+                                     int32_t D, const flex_block_mask* bm) {
+    if (!bm || B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || L >= kMaxLen || S >= kMaxLen || Hq % Hkv) return 0;
+    if ((dtype != FLEX_F32 && dtype != FLEX_BF16) || (D != 64 && D != 128)) return 0;
+    return attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block,
+                                    bm->num_kv_blocks, bm->B, bm->H);
+}
+
+flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                          int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                          const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                          const flex_score_params* score, const flex_mask_params* mask, const flex_block_mask* bm,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
+                                  bm, out, lse))
+        return s;
+    if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
+    const size_t need = attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block,
+                                                 bm->num_kv_blocks, bm->B, bm->H);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(FLEX_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (need > 0 && !aligned16(workspace)) return fail(FLEX_ERR_LAYOUT, "workspace must be 16-byte aligned");
+
+    FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.q_sb = q_strides[0]; a.q_sh = q_strides[1]; a.q_sr = q_strides[2];
+    a.k_sb = k_strides[0]; a.k_sh = k_strides[1]; a.k_sr = k_strides[2];
+    a.v_sb = v_strides[0]; a.v_sh = v_strides[1]; a.v_sr = v_strides[2];
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = (int)L;
+    a.S = (int)S;
+    a.group = Hq / Hkv;
+    a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+    a.score_kind = score->kind;
+    a.cap = score->kind == FLEX_SCORE_NONE ? 1.0f : score->cap;
+    a.alibi_m = score->alibi_m;
+    a.mask = to_mask_args(mask);
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    a.Bm = bm->B;
+    a.Hm = bm->H;
+    a.nQB = bm->num_q_blocks;
+    a.nKB = bm->num_kv_blocks;
+    a.q_block = bm->q_block;
+    a.kv_block = bm->kv_block;
+    a.ws_acc = nullptr;
+    a.ws_ml = nullptr;
+    a.splits = 1;
+    if (need > 0) {
+        a.ws_acc = reinterpret_cast<float*>(workspace);
+    }
+    (void)hipGetLastError();
+    hipError_t e = launch_attn_fwd(dtype, D, a, as_stream(stream));
+    if (e != hipSuccess) return fail(FLEX_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    return FLEX_OK;
+}
+
+}  // extern "C"

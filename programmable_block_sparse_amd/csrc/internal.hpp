@@ -1,0 +1,64 @@
+// Internal launch interfaces between the C-ABI layer (flexmi_api.hip) and the
+// kernel translation units.  Everything here has been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace flexmi {
+
+struct BuildArgs {
+    MaskArgs mask;
+    int L, S;
+    int q_block, kv_block;
+    int nQB, nKB;
+    int Bm, Hm;
+    int* kv_num;
+    int* kv_idx;
+    int* full_num;
+    int* full_idx;
+};
+
+hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream);
+
+// Forward pass arguments (element strides; last dim contiguous).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int B, Hq, Hkv, L, S, group;
+    float scale;
+    // score_mod
+    int score_kind;
+    float cap;
+    float alibi_m;
+    // mask_mod
+    MaskArgs mask;
+    // block mask
+    const int* kv_num;
+    const int* kv_idx;
+    const int* full_num;
+    const int* full_idx;
+    int Bm, Hm, nQB, nKB, q_block, kv_block;
+    // split-KV decode
+    float* ws_acc;      // [splits][B][Hq][L][D] partial numerators
+    float* ws_ml;       // [splits][B][Hq][L][2]  partial (reference, denominator)
+    int splits;
+};
+
+// dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for an unsupported
+// combination (the host validated the combination before).
+hipError_t launch_attn_fwd(int dtype, int D, const FwdArgs& a, hipStream_t stream);
+
+// Workspace bytes for the split-KV path; 0 when the prefill kernel is used.
+size_t attn_fwd_workspace_bytes(int dtype, int B, int Hq, int Hkv, int L, int S, int D,
+                                int q_block, int kv_block, int nKB, int Bm, int Hm);
+
+}  // namespace flexmi

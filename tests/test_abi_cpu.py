@@ -1,0 +1,189 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/flexmi.h, and rejects each kind of invalid argument with
+its status code before any HIP call is made (the pointers below are fake
+16-byte-aligned addresses that are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import programmable_block_sparse_amd as pbs
+from programmable_block_sparse_amd import flex_block_mask, flex_mask_params, flex_score_params
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flexmi.h")
+
+FAKE = 0x10000   # aligned, never dereferenced
+OK, NULL, SHAPE, GQA, BLOCKMASK, UNSUPPORTED, LAYOUT, WORKSPACE, HIP, PARAM = range(10)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pbs.library_path()):
+        pytest.skip("libflexmi.so not built")
+    return pbs.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flex_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(pbs.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pbs.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (flex_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    names = ["FLEX_OK", "FLEX_ERR_NULL", "FLEX_ERR_SHAPE", "FLEX_ERR_GQA", "FLEX_ERR_BLOCKMASK",
+             "FLEX_ERR_UNSUPPORTED", "FLEX_ERR_LAYOUT", "FLEX_ERR_WORKSPACE", "FLEX_ERR_HIP", "FLEX_ERR_PARAM"]
+    for code, name in enumerate(names):
+        assert pbs.flex_status_string(code) == name
+    assert pbs.flex_status_string(99) == "FLEX_ERR_UNKNOWN"
+
+
+def _bm(L, S, qb, kb, B=1, H=1):
+    c = flex_block_mask()
+    c.B, c.H, c.q_block, c.kv_block = B, H, qb, kb
+    c.num_q_blocks, c.num_kv_blocks = -(-L // qb), -(-S // kb)
+    c.kv_num_blocks = c.kv_indices = c.full_kv_num_blocks = c.full_kv_indices = FAKE
+    return c
+
+
+def _mask(kind="causal", q_offset=0, window=0, sinks=0, doc=None, doc_len=0):
+    m = flex_mask_params()
+    m.kind, m.q_offset, m.window, m.sinks = pbs.MASK_KINDS[kind], q_offset, window, sinks
+    m.doc_id, m.doc_len = doc, doc_len
+    return m
+
+
+def _score(kind="none", cap=0.0, alibi_m=8.0):
+    s = flex_score_params()
+    s.kind, s.cap, s.alibi_m = pbs.SCORE_KINDS[kind], cap, alibi_m
+    return s
+
+
+def build(lib, mask, L, S, bm):
+    return lib.flex_blockmask_build(ctypes.byref(mask) if mask is not None else None, L, S,
+                                    ctypes.byref(bm) if bm is not None else None, None)
+
+
+def test_builder_rejects(lib):
+    L = S = 256
+    assert build(lib, None, L, S, _bm(L, S, 64, 64)) == NULL
+    assert build(lib, _mask(), L, S, None) == NULL
+    bad = _bm(L, S, 64, 64); bad.kv_indices = None
+    assert build(lib, _mask(), L, S, bad) == NULL
+    assert build(lib, _mask(), 0, S, _bm(1, S, 64, 64)) == SHAPE
+    assert build(lib, _mask(), L, 1 << 30, _bm(L, 1 << 20, 64, 64)) == SHAPE
+    small = _bm(L, S, 64, 64); small.num_q_blocks = 3
+    assert build(lib, _mask(), L, S, small) == BLOCKMASK
+    assert "too small" in pbs.flex_last_error()
+    large = _bm(L, S, 64, 64); large.num_kv_blocks = 5
+    assert build(lib, _mask(), L, S, large) == BLOCKMASK
+    assert "too large" in pbs.flex_last_error()
+    assert build(lib, _mask(), L, S, _bm(L, S, 2048, 64)) == BLOCKMASK
+    assert build(lib, _mask(), L, S, _bm(L, S, 64, 64, B=0)) == BLOCKMASK
+    m = _mask(); m.kind = 7
+    assert build(lib, m, L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("causal_window_sinks", window=0), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("causal_window_sinks", window=4, sinks=-1), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("doc_causal", doc=None), L, S, _bm(L, S, 64, 64)) == NULL
+    assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S - 1), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S, q_offset=-1), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S, q_offset=5), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask(q_offset=1 << 30), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask(), 64, 64 * 70000, _bm(64, 64 * 70000, 64, 64)) == UNSUPPORTED
+
+
+class Fwd:
+    """Valid argument set for flex_attn_fwd; tests change one thing at a time."""
+
+    def __init__(self, dtype=1, B=2, Hq=4, Hkv=2, L=256, S=256, D=64, qb=128, kb=64):
+        self.q = self.k = self.v = self.out = FAKE
+        self.lse = FAKE
+        self.dtype, self.B, self.Hq, self.Hkv, self.L, self.S, self.D = dtype, B, Hq, Hkv, L, S, D
+        self.qs = [Hq * L * D, L * D, D]
+        self.ks = [Hkv * S * D, S * D, D]
+        self.vs = list(self.ks)
+        self.scale = 0.0
+        self.score = _score("softcap", cap=30.0)
+        self.mask = _mask("causal", q_offset=S - L)
+        self.bm = _bm(L, S, qb, kb)
+        self.ws, self.ws_bytes = None, 0
+
+    def call(self, lib):
+        a3 = lambda x: None if x is None else (ctypes.c_int64 * 3)(*x)
+        ref = lambda x: None if x is None else ctypes.byref(x)
+        return lib.flex_attn_fwd(self.q, self.k, self.v, self.dtype, self.B, self.Hq, self.Hkv, self.L, self.S,
+                                 self.D, a3(self.qs), a3(self.ks), a3(self.vs), ctypes.c_float(self.scale),
+                                 ref(self.score), ref(self.mask), ref(self.bm), self.out, self.lse, self.ws,
+                                 self.ws_bytes, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (lambda f: setattr(f, "q", None), NULL),
+    (lambda f: setattr(f, "out", None), NULL),
+    (lambda f: setattr(f, "ks", None), NULL),
+    (lambda f: setattr(f, "score", None), NULL),
+    (lambda f: setattr(f, "mask", None), NULL),
+    (lambda f: setattr(f, "bm", None), NULL),
+    (lambda f: setattr(f.bm, "full_kv_indices", None), NULL),
+    (lambda f: setattr(f, "B", 0), SHAPE),
+    (lambda f: setattr(f, "L", -3), SHAPE),
+    (lambda f: setattr(f, "Hkv", 3), GQA),
+    (lambda f: setattr(f, "dtype", 2), UNSUPPORTED),
+    (lambda f: setattr(f, "D", 96), UNSUPPORTED),
+    (lambda f: setattr(f.bm, "num_q_blocks", 1), BLOCKMASK),
+    (lambda f: setattr(f.bm, "num_kv_blocks", 8), BLOCKMASK),
+    (lambda f: setattr(f.bm, "B", 3), BLOCKMASK),
+    (lambda f: setattr(f.bm, "H", 2), BLOCKMASK),
+    (lambda f: (setattr(f.bm, "q_block", 48), setattr(f.bm, "num_q_blocks", 6)), UNSUPPORTED),
+    (lambda f: (setattr(f.bm, "kv_block", 32), setattr(f.bm, "num_kv_blocks", 8)), UNSUPPORTED),
+    (lambda f: setattr(f, "q", FAKE + 8), LAYOUT),
+    (lambda f: setattr(f, "out", FAKE + 4), LAYOUT),
+    (lambda f: setattr(f, "lse", FAKE + 2), LAYOUT),
+    (lambda f: setattr(f, "qs", [1 << 20, 1 << 14, 66]), LAYOUT),
+    (lambda f: setattr(f, "ks", [-64, 64, 64]), LAYOUT),
+    (lambda f: setattr(f, "score", _score("softcap", cap=0.0)), PARAM),
+    (lambda f: setattr(f, "score", _score("softcap_alibi", cap=float("inf"))), PARAM),
+    (lambda f: setattr(f.score, "kind", 5), PARAM),
+    (lambda f: setattr(f.mask, "kind", -1), PARAM),
+    (lambda f: setattr(f, "mask", _mask("causal_window_sinks", window=0)), PARAM),
+    (lambda f: setattr(f, "mask", _mask("doc_causal", doc=None)), NULL),
+    (lambda f: setattr(f, "mask", _mask("doc_causal", doc=FAKE, doc_len=100)), PARAM),
+    (lambda f: setattr(f, "mask", _mask("doc_causal", doc=FAKE + 2, doc_len=256)), LAYOUT),
+    (lambda f: setattr(f, "scale", float("inf")), PARAM),
+])
+def test_fwd_rejects(lib, change, code):
+    f = Fwd()
+    change(f)
+    assert f.call(lib) == code, pbs.flex_last_error()
+    assert pbs.flex_last_error() != ""
+
+
+def test_fp32_alignment_unit_is_four_elements(lib):
+    f = Fwd(dtype=0)
+    f.qs = [f.Hq * f.L * 68, f.L * 68, 68]        # 68 floats = 272 bytes: aligned for fp32 ...
+    f.q = FAKE + 16
+    f.mask = _mask("causal_window_sinks", window=0)  # ... so the first failure is the mask
+    assert f.call(lib) == PARAM
+    f.qs = [f.Hq * f.L * 66, f.L * 66, 66]
+    assert f.call(lib) == LAYOUT
+
+
+def test_workspace_query_rejects_bad_shapes(lib):
+    bm = _bm(256, 256, 128, 64)
+    assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 3, 256, 256, 64, ctypes.byref(bm)) == 0
+    assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 2, 256, 256, 96, ctypes.byref(bm)) == 0
+    assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 2, 256, 256, 64, None) == 0

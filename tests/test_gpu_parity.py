@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+BlockMask arrays must match bit for bit; out within 2e-2 (bf16 inputs) or
+1e-5 (fp32) max-abs; lse within 1e-3 and -inf exactly where the oracle has it.
+Small cases compare every output; the five full-size workloads compare sampled
+rows (edges of every Q block plus random rows) that the oracle computes one by
+one.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import programmable_block_sparse_amd as pbs
+from gpu_common import (assert_attention_close, assert_block_mask_equal, oracle_mods, require_gpu)
+from oracle import MaskMod, ScoreMod, attention, build_block_mask
+from workloads import (WORKLOAD_ORDER, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
+                       workload_doc_ids)
+from workloads.torch_io import specs, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _mask_pair(kind, window=0, sinks=0, q_offset=0, doc_np=None, doc_t=None):
+    return (pbs.MaskSpec(kind=kind, window=window, sinks=sinks, q_offset=q_offset, doc_id=doc_t),
+            MaskMod(kind, window=window, sinks=sinks, doc_id=doc_np))
+
+
+def _rand_doc(rng, n):
+    cuts = np.sort(rng.choice(np.arange(1, n), size=min(n - 1, int(rng.integers(0, 5))), replace=False)) if n > 1 else []
+    lens = np.diff(np.concatenate([[0], cuts, [n]])).astype(np.int64)
+    return np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+
+
+# ------------------------------------------------------------ BlockMask builder
+def test_blockmask_fuzz_bit_exact(dev):
+    rng = np.random.default_rng(1234)
+    kinds = ["noop", "causal", "causal_window_sinks", "doc_causal"]
+    n_cases = 0
+    for trial in range(160):
+        L, S = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        QB = int(rng.choice([1, 2, 3, 4, 7, 16, 32, 64, 128]))
+        KB = int(rng.choice([1, 2, 5, 16, 64, 128]))
+        kind = kinds[trial % 4]
+        offs = [S - L, 0, int(rng.integers(-40, 40))]
+        for off in offs:
+            doc_np = doc_t = None
+            if kind == "doc_causal":
+                if off < 0:
+                    continue
+                doc_np = _rand_doc(rng, max(S, off + L) + int(rng.integers(0, 3)))
+                doc_t = torch.from_numpy(doc_np).to(dev)
+            window, sinks = int(rng.integers(1, 40)), int(rng.integers(0, 6))
+            spec, mod = _mask_pair(kind, window, sinks, off, doc_np, doc_t)
+            Bm, Hm = (1, 1) if trial % 3 else (2, 3)
+            gpu = pbs.flex_blockmask_build(spec, L, S, QB, KB, B=Bm, H=Hm, device=dev)
+            ref = build_block_mask(mod, L, S, QB, KB, B=Bm, H=Hm, q_offset=off)
+            assert_block_mask_equal(gpu, ref)
+            n_cases += 1
+    assert n_cases > 300
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_blockmask_workloads_bit_exact(dev, name):
+    w = WORKLOADS[name]
+    doc_np = workload_doc_ids(w)
+    doc_t = torch.from_numpy(doc_np).to(dev) if doc_np is not None else None
+    spec, _ = specs(w, doc_t)
+    mod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=doc_np)
+    gpu = pbs.flex_blockmask_build(spec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    ref = build_block_mask(mod, w.L, w.S, w.q_block, w.kv_block, q_offset=w.q_offset)
+    assert_block_mask_equal(gpu, ref)
+
+
+# ------------------------------------------------------- attention, small cases
+def _tensor(x_f32, dtype, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(f32_to_bf16_bits(x_f32).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32)).to(dev)
+
+
+def _widen(x_f32, dtype):
+    return bf16_bits_to_f32(f32_to_bf16_bits(x_f32)) if dtype == "bf16" else x_f32
+
+
+def run_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_kind, window=0, sinks=0,
+             q_offset=None, value_scale=1.0, scale=None, with_lse=True, what=""):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32) * np.float32(value_scale)
+    off = S - L if q_offset is None else q_offset
+    doc_np = doc_t = None
+    if mask_kind == "doc_causal":
+        doc_np = _rand_doc(rng, max(S, off + L))
+        doc_t = torch.from_numpy(doc_np).to(dev)
+    mspec, mmod = _mask_pair(mask_kind, window, sinks, off, doc_np, doc_t)
+    sspec = pbs.ScoreSpec(**score)
+    smod = ScoreMod(**score)
+    bm = pbs.flex_blockmask_build(mspec, L, S, qb, kb, device=dev)
+    out, lse = pbs.flex_attn_fwd(_tensor(q, dtype, dev), _tensor(k, dtype, dev), _tensor(v, dtype, dev),
+                                 block_mask=bm, score=sspec, mask=mspec, scale=scale, return_lse=with_lse)
+    torch.cuda.synchronize()
+    sc = pbs.default_scale(D) if scale is None else float(np.float32(scale))
+    out_ref, lse_ref = attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale=sc, score=smod,
+                                 mask=mmod, q_offset=off)
+    return assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
+
+
+SCORES = [dict(kind="none"), dict(kind="softcap", cap=5.0), dict(kind="softcap_alibi", cap=30.0, alibi_m=8.0)]
+MASKS = [dict(mask_kind="noop"), dict(mask_kind="causal"),
+         dict(mask_kind="causal_window_sinks", window=70, sinks=3), dict(mask_kind="doc_causal")]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_attention_menu_small(dev, dtype, D):
+    """Every score x mask pair on ragged lengths that span several tiles."""
+    for i, (score, mask) in enumerate(itertools.product(SCORES, MASKS)):
+        L, S = (300, 300) if i % 2 == 0 else (173, 389)
+        run_case(dev, seed=100 + i, dtype=dtype, B=2, Hq=4, Hkv=2, L=L, S=S, D=D, qb=128, kb=64, score=score,
+                 what=f"{dtype} D={D} {score} {mask}", **mask)
+
+
+@pytest.mark.parametrize("qb,kb", [(16, 64), (32, 64), (64, 64), (64, 128), (128, 128), (128, 192)])
+def test_attention_tile_shapes(dev, qb, kb):
+    for dtype in ("bf16", "f32"):
+        run_case(dev, seed=7 + qb + kb, dtype=dtype, B=1, Hq=2, Hkv=1, L=211, S=333, D=64, qb=qb, kb=kb,
+                 score=dict(kind="softcap_alibi", cap=20.0), mask_kind="causal", what=f"{dtype} {qb}x{kb}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_attention_gqa_ratios(dev, G):
+    run_case(dev, seed=40 + G, dtype="bf16", B=2, Hq=8, Hkv=8 // G, L=150, S=150, D=128, qb=128, kb=64,
+             score=dict(kind="softcap", cap=50.0), mask_kind="causal_window_sinks", window=40, sinks=4,
+             what=f"G={G}")
+
+
+def test_attention_empty_rows_and_offsets(dev):
+    # L > S bottom-right: the first L - S rows see no key -> out 0, lse -inf
+    run_case(dev, seed=3, dtype="bf16", B=1, Hq=2, Hkv=2, L=200, S=70, D=64, qb=64, kb=64,
+             score=dict(kind="softcap", cap=10.0), mask_kind="causal", what="L>S")
+    run_case(dev, seed=4, dtype="f32", B=1, Hq=2, Hkv=1, L=100, S=30, D=128, qb=32, kb=64,
+             score=dict(kind="none"), mask_kind="causal", what="L>S f32")
+    # negative and top-left offsets
+    for off in (0, -17, 45):
+        run_case(dev, seed=5, dtype="bf16", B=1, Hq=2, Hkv=1, L=90, S=260, D=64, qb=32, kb=64,
+                 score=dict(kind="softcap_alibi", cap=30.0), mask_kind="causal", q_offset=off, what=f"off={off}")
+    # window 1 (only self) and sinks only
+    run_case(dev, seed=6, dtype="bf16", B=1, Hq=1, Hkv=1, L=130, S=130, D=64, qb=128, kb=64,
+             score=dict(kind="none"), mask_kind="causal_window_sinks", window=1, sinks=0, what="w=1")
+    run_case(dev, seed=6, dtype="bf16", B=1, Hq=1, Hkv=1, L=130, S=130, D=64, qb=128, kb=64,
+             score=dict(kind="none"), mask_kind="causal_window_sinks", window=1, sinks=64, what="sinks")
+
+
+def test_attention_minimum_sizes(dev):
+    for L, S in ((1, 1), (1, 65), (17, 1), (2, 3)):
+        for dtype in ("bf16", "f32"):
+            run_case(dev, seed=L * 100 + S, dtype=dtype, B=1, Hq=1, Hkv=1, L=L, S=S, D=64, qb=16, kb=64,
+                     score=dict(kind="softcap", cap=5.0), mask_kind="causal", what=f"L={L} S={S}")
+
+
+def test_attention_large_scores_and_values(dev):
+    # sharper softmax (scale 1) and large values exercise the rescale path and the bf16 budget
+    run_case(dev, seed=9, dtype="f32", B=1, Hq=2, Hkv=2, L=256, S=256, D=64, qb=64, kb=64,
+             score=dict(kind="none"), mask_kind="causal", scale=1.0, what="scale 1 f32")
+    run_case(dev, seed=9, dtype="bf16", B=1, Hq=2, Hkv=2, L=256, S=256, D=64, qb=128, kb=64,
+             score=dict(kind="softcap", cap=50.0), mask_kind="noop", scale=2.0, what="scale 2 bf16")
+    run_case(dev, seed=10, dtype="bf16", B=1, Hq=2, Hkv=2, L=256, S=256, D=128, qb=128, kb=64,
+             score=dict(kind="none"), mask_kind="causal", value_scale=0.5, what="values")
+
+
+def test_lse_optional_and_strided_inputs(dev):
+    rng = np.random.default_rng(11)
+    B, H, L, S, D = 2, 4, 190, 190, 64
+    qkv = rng.standard_normal((3, B, L, H, D), dtype=np.float32)       # (B, L, H, D) storage
+    t = _tensor(qkv, "bf16", dev)
+    q, k, v = (t[i].permute(0, 2, 1, 3) for i in range(3))              # (B, H, L, D) views, strided
+    mspec = pbs.MaskSpec(kind="causal")
+    sspec = pbs.ScoreSpec(kind="softcap_alibi", cap=30.0)
+    bm = pbs.flex_blockmask_build(mspec, L, S, 128, 64, device=dev)
+    out_s, lse_s = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    out_c, lse_c = pbs.flex_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), block_mask=bm, score=sspec,
+                                     mask=mspec)
+    out_n, lse_n = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse_n is None
+    assert torch.equal(out_s, out_c) and torch.equal(lse_s, lse_c) and torch.equal(out_s, out_n)
+
+
+# ------------------------------------------------- the five full-size workloads
+def _sample_rows(w: Workload, rng, n_random=48):
+    edges = set()
+    for qb in range(-(-w.L // w.q_block)):
+        for r in (qb * w.q_block, qb * w.q_block + w.q_block - 1):
+            if 0 <= r < w.L:
+                edges.add(r)
+    rows = sorted(edges | set(rng.integers(0, w.L, size=min(n_random, w.L)).tolist()) | {0, w.L - 1})
+    if len(rows) > 96:
+        rows = sorted(set(rng.choice(rows, size=96, replace=False).tolist()) | {0, w.L - 1})
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_parity_sampled(dev, name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    q, k, v, doc_t = to_device(w, inp, dev)
+    mspec, sspec = specs(w, doc_t)
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    out, lse = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    torch.cuda.synchronize()
+    out_np = out.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    mmod, smod = oracle_mods(w, inp["doc_id"])
+    rng = np.random.default_rng(w.seed)
+    if w.B * w.Hq * w.L <= 1024:            # small workload: every output
+        bs, hs, rows = range(w.B), range(w.Hq), np.arange(w.L)
+    else:
+        bs = sorted({0, w.B - 1})
+        hs = sorted({0, w.Hq - 1, int(rng.integers(0, w.Hq))})
+        rows = _sample_rows(w, rng)
+    out_ref, lse_ref = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod,
+                                 mask=mmod, q_offset=w.q_offset, rows=rows, heads=hs, batches=bs)
+    got_o = out_np[np.ix_(list(bs), list(hs), rows)]
+    got_l = lse_np[np.ix_(list(bs), list(hs), rows)]
+    assert_attention_close(got_o, got_l, out_ref, lse_ref, w.dtype, name)
+    # properties that hold at any size: finite everywhere rows see keys, no NaN
+    assert not np.isnan(out_np).any() and not np.isnan(lse_np).any()
+
+
+def test_run_to_run_bitwise_determinism(dev):
+    w = WORKLOADS["causal_softcap_alibi"]
+    inp = make_inputs(w)
+    q, k, v, _ = to_device(w, inp, dev)
+    mspec, sspec = specs(w)
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    o1, l1 = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    o2, l2 = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

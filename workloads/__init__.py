@@ -28,26 +28,33 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "draw_doc_lengths", "doc_ids_from_lengths",
-    "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits", "make_inputs",
+    "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits", "make_inputs", "workload_doc_ids", "WORKLOAD_ORDER",
 ]
 
 
-def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+def f32_to_bf16_bits(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
 
+    Works in uint32 (no overflow for finite inputs: the largest finite pattern
+    plus the rounding bias stays below 2^32) and in chunks to bound memory.
     Inputs here are finite by construction; NaN payloads are not handled.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for i in range(0, flat.size, chunk):
+        u = flat[i:i + chunk]
+        r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        out[i:i + chunk] = (r >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) -> exactly widened float32."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out = np.empty(b.shape, dtype=np.uint32)
+    np.left_shift(b, 16, out=out, dtype=np.uint32)
+    return out.view(np.float32)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -115,6 +122,14 @@ WORKLOAD_ORDER = ["causal_f32", "causal_softcap_alibi", "doc_causal", "window_si
 
 def get_workload(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def workload_doc_ids(w: Workload):
+    """The packed-document workload's doc_id array (same draw as make_inputs), or None."""
+    if not w.docs:
+        return None
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    return doc_ids_from_lengths(draw_doc_lengths(rng, w.S))
 
 
 def make_inputs(w: Workload, *, B: Optional[int] = None, seed: Optional[int] = None) -> dict:
