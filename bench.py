@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="causal_softcap_alibi")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
     return p.parse_args()
 
@@ -89,19 +90,20 @@ def main():
     ws_bytes = pbs.flex_attn_fwd_workspace_bytes(q.dtype, w.B, w.Hq, w.Hkv, w.L, w.S, w.D, bm)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+    bm_step = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+
     def fwd():
         pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
 
-    def step():
-        b2 = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
-        pbs.flex_attn_fwd(q, k, v, block_mask=b2, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
-
     def build_only():
-        pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+        pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, out=bm_step)
 
-    stream = torch.cuda.current_stream(dev)
+    def step():
+        build_only()
+        pbs.flex_attn_fwd(q, k, v, block_mask=bm_step, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
 
     def timed(fn, n):
+        stream = torch.cuda.current_stream(dev)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
@@ -115,11 +117,39 @@ def main():
         step()
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    ms_step = timed(step, args.steps)
-    ms_fwd = timed(fwd, args.steps)
-    ms_mask = timed(build_only, args.steps)
-    print(f"bench: step {ms_step * 1e3:.1f} us, fwd {ms_fwd * 1e3:.1f} us, block mask {ms_mask * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    mode = "eager"
+    runners = {"step": step, "fwd": fwd, "mask": build_only}
+    if not args.eager:
+        # One HIP graph per measured unit, replayed back to back.  Each replay is
+        # checked against the eager result (the graph holds only our kernels).
+        out_ref, lse_ref = out.clone(), lse.clone()
+        graphs = {}
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for name, fn in runners.items():
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    fn()
+                graphs[name] = g
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(3):
+            out.zero_()
+            lse.zero_()
+            graphs["step"].replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(out, out_ref) and torch.equal(lse, lse_ref)):
+                raise RuntimeError(f"graph replay {i} differs from the eager result")
+            step()                       # eager work between replays
+            torch.cuda.synchronize()
+        runners = {name: g.replay for name, g in graphs.items()}
+        mode = "hip_graph"
+    ms_step = timed(runners["step"], args.steps)
+    ms_fwd = timed(runners["fwd"], args.steps)
+    ms_mask = timed(runners["mask"], args.steps)
+    print(f"bench: step {ms_step * 1e3:.1f} us, fwd {ms_fwd * 1e3:.1f} us, block mask {ms_mask * 1e3:.1f} us "
+          f"({mode})", file=sys.stderr, flush=True)
 
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
@@ -131,7 +161,7 @@ def main():
         roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = "attn_fwd_prefill"
+    roof["kernel"] = "attn_fwd_decode + attn_fwd_combine" if ws_bytes else "attn_fwd_prefill"
     roof["algorithmic_per_launch"] = flops if roof["unit"] == "TFLOP/s" else alg_bytes
 
     result = {
@@ -144,7 +174,7 @@ def main():
                    "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset,
                    "doc_lengths": inp["doc_lengths"]},
         "roofline": roof,
-        "fwd_ms": ms_fwd, "blockmask_ms": ms_mask,
+        "fwd_ms": ms_fwd, "blockmask_ms": ms_mask, "launch_mode": mode,
         "fwd_tflops_visited": fwd_tflops, "pct_bf16_peak_fwd": 100.0 * fwd_tflops / BF16_PEAK_TFLOPS,
         "visited_block_flops": flops, "algorithmic_bytes": alg_bytes,
         "hbm_gbs_fwd": alg_bytes / (ms_fwd * 1e-3) / 1e9,

@@ -118,6 +118,11 @@ class MaskSpec:
     doc_id: Optional[torch.Tensor] = None   # int32 device tensor for "doc_causal"
 
     def to_c(self, L: int, S: int) -> flex_mask_params:
+        key = (L, S, self.kind, self.window, self.sinks, self.q_offset,
+               None if self.doc_id is None else (self.doc_id.data_ptr(), self.doc_id.numel()))
+        cached = self.__dict__.get("_c")
+        if cached is not None and cached[0] == key:
+            return cached[1]
         m = flex_mask_params()
         m.kind = MASK_KINDS[self.kind]
         m.window = int(self.window)
@@ -128,6 +133,7 @@ class MaskSpec:
                 raise ValueError("doc_id must be a contiguous int32 tensor")
             m.doc_id = self.doc_id.data_ptr()
             m.doc_len = self.doc_id.numel()
+        self.__dict__["_c"] = (key, m)
         return m
 
 
@@ -139,10 +145,15 @@ class ScoreSpec:
     alibi_m: float = 8.0
 
     def to_c(self) -> flex_score_params:
+        key = (self.kind, self.cap, self.alibi_m)
+        cached = self.__dict__.get("_c")
+        if cached is not None and cached[0] == key:
+            return cached[1]
         s = flex_score_params()
         s.kind = SCORE_KINDS[self.kind]
         s.cap = float(self.cap)
         s.alibi_m = float(self.alibi_m)
+        self.__dict__["_c"] = (key, s)
         return s
 
 
@@ -167,6 +178,9 @@ class BlockMask:
         return self.kv_num_blocks.shape[1]
 
     def to_c(self) -> flex_block_mask:
+        cached = self.__dict__.get("_c")
+        if cached is not None:
+            return cached
         c = flex_block_mask()
         c.B, c.H = self.B, self.H
         c.q_block, c.kv_block = self.q_block, self.kv_block
@@ -175,6 +189,7 @@ class BlockMask:
         c.kv_indices = self.kv_indices.data_ptr()
         c.full_kv_num_blocks = self.full_kv_num_blocks.data_ptr()
         c.full_kv_indices = self.full_kv_indices.data_ptr()
+        self.__dict__["_c"] = c
         return c
 
 
@@ -183,17 +198,25 @@ def _stream_ptr(device) -> int:
 
 
 def flex_blockmask_build(mask: MaskSpec, L: int, S: int, q_block: int, kv_block: int, *, B: int = 1, H: int = 1,
-                         device="cuda") -> BlockMask:
-    """Allocate the BlockMask tensors and fill them on the GPU (C: flex_blockmask_build)."""
+                         device="cuda", out: Optional[BlockMask] = None) -> BlockMask:
+    """Fill a BlockMask on the GPU (C: flex_blockmask_build).
+
+    Allocates the four int32 tensors unless ``out`` (a BlockMask of the same dims)
+    is given, in which case it is refilled in place.
+    """
     lib = load_library()
-    nqb, nkb = -(-L // q_block), -(-S // kv_block)
-    dev = torch.device(device)
-    t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
-    bm = BlockMask(t(B, H, nqb), t(B, H, nqb, nkb), t(B, H, nqb), t(B, H, nqb, nkb), q_block, kv_block, L, S)
+    if out is None:
+        nqb, nkb = -(-L // q_block), -(-S // kv_block)
+        dev = torch.device(device)
+        t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+        out = BlockMask(t(B, H, nqb), t(B, H, nqb, nkb), t(B, H, nqb), t(B, H, nqb, nkb), q_block, kv_block, L, S)
+    elif (out.L, out.S, out.q_block, out.kv_block, out.B, out.H) != (L, S, q_block, kv_block, B, H):
+        raise ValueError("out BlockMask has different dims")
     cm = mask.to_c(L, S)
-    cbm = bm.to_c()
-    _check(lib.flex_blockmask_build(ctypes.byref(cm), L, S, ctypes.byref(cbm), ctypes.c_void_p(_stream_ptr(dev))))
-    return bm
+    cbm = out.to_c()
+    _check(lib.flex_blockmask_build(ctypes.byref(cm), L, S, ctypes.byref(cbm),
+                                    ctypes.c_void_p(_stream_ptr(out.kv_num_blocks.device))))
+    return out
 
 
 def flex_attn_fwd_workspace_bytes(dtype: torch.dtype, B: int, Hq: int, Hkv: int, L: int, S: int, D: int,

@@ -31,6 +31,9 @@ def compile_flags() -> list:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from forming packed-fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the score tiles are consumed by
+        # VALU right away, so AGPR round trips would only cost moves
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     ]
 

@@ -6,8 +6,16 @@
 // section 4.1: create_block_mask with full tiles kept in their own lists) and
 // the charlestar blog "FlexAttention score_mod / BlockMask" (BlockMask
 // section: empty / full / partial tiles).  Unlike the eager path the blog's
-// cache section describes, no element-level dense mask is materialised: each
-// wave counts visible cells of one tile in registers.
+// cache section describes, no element-level dense mask is materialised.
+//
+// Two launches on the caller's stream:
+//   classify  one wave per tile; each lane owns a key column and the wave
+//             walks the tile's rows, so one v_cmp + ballot evaluates 64 cells
+//             and the visible-cell count accumulates in scalar registers.  The
+//             tile class (0 empty, 1 partial, 2 full) is parked in the tile's
+//             own kv_indices slot.
+//   compact   one workgroup per Q-block row reads the row's classes into LDS
+//             and rewrites kv_indices / full_kv_indices as ordered lists.
 //
 // Layout conventions: cells beyond L or S are not visible; each index row
 // lists its tiles ascending, then the remaining tile indices ascending.
@@ -17,48 +25,77 @@ namespace flexmi {
 
 namespace {
 
-constexpr int kBuildThreads = 512;
-constexpr int kBuildWaves = kBuildThreads / 64;
+constexpr int kClassifyWaves = 8;
+constexpr int kCompactThreads = 256;
 
-enum : uint8_t { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
+enum : int { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
 
-__global__ __launch_bounds__(kBuildThreads) void blockmask_build_kernel(BuildArgs a) {
+// Ballot of the visible cells of one query position p over this lane's key
+// column (branch-free within the row; col_ok folds the tile and S bounds).
+template <int KIND>
+__device__ __forceinline__ uint64_t row_ballot(const MaskArgs& m, int p, int col, bool col_ok, int doc_p,
+                                               int doc_col) {
+    bool v;
+    if constexpr (KIND == MASK_NOOP) {
+        v = col_ok;
+    } else if constexpr (KIND == MASK_CAUSAL) {
+        v = col_ok & (col <= p);
+    } else if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS) {
+        v = col_ok & (col <= p) & ((p - col < m.window) | (col < m.sinks));
+    } else {
+        v = col_ok & (col <= p) & (doc_p == doc_col);
+    }
+    return __ballot(v);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kClassifyWaves * 64) void blockmask_classify(BuildArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int kb = blockIdx.x * kClassifyWaves + (threadIdx.x >> 6);
+    if (kb >= a.nKB) return;
+    const int qb = blockIdx.y;
+    const int bh = blockIdx.z;
+    const int row0 = qb * a.q_block;
+    const int rows = min(a.q_block, a.L - row0);
+    const int64_t row_id = (int64_t)bh * a.nQB + qb;
+    int64_t count = 0;
+    for (int j0 = 0; j0 < a.kv_block; j0 += 64) {
+        const int jj = j0 + lane;
+        const int col = kb * a.kv_block + jj;
+        const bool col_ok = (jj < a.kv_block) & (col < a.S);
+        int doc_col = -1;
+        if constexpr (KIND == MASK_DOC_CAUSAL)
+            doc_col = (col_ok && col < a.mask.doc_len) ? __ldg(a.mask.doc_id + col) : -1;
+        for (int i = 0; i < rows; ++i) {
+            const int p = row0 + i + a.mask.q_offset;
+            int doc_p = -2;
+            if constexpr (KIND == MASK_DOC_CAUSAL)
+                doc_p = (p >= 0 && p < a.mask.doc_len) ? __ldg(a.mask.doc_id + p) : -2;
+            count += __popcll(row_ballot<KIND>(a.mask, p, col, col_ok, doc_p, doc_col));
+        }
+    }
+    if (lane == 0) {
+        const int64_t cells = (int64_t)a.q_block * a.kv_block;
+        a.kv_idx[row_id * a.nKB + kb] = count == 0 ? TILE_EMPTY : (count == cells ? TILE_FULL : TILE_PARTIAL);
+    }
+}
+
+__global__ __launch_bounds__(kCompactThreads) void blockmask_compact(BuildArgs a) {
     extern __shared__ uint8_t tile_class[];  // [nKB]
     const int qb = blockIdx.x;
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    const int bh = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int row0 = qb * a.q_block;
-    const int cells = a.q_block * a.kv_block;
-
-    // Phase 1: one wave per tile; lanes sweep the tile row by row.
-    for (int kb = wave; kb < a.nKB; kb += kBuildWaves) {
-        const int col0 = kb * a.kv_block;
-        int count = 0;
-        for (int i = 0; i < a.q_block; ++i) {
-            const int row = row0 + i;
-            const bool row_in = row < a.L;
-            const int p = row + a.mask.q_offset;
-            for (int j0 = 0; j0 < a.kv_block; j0 += 64) {
-                const int jj = j0 + lane;
-                const int col = col0 + jj;
-                const bool vis = row_in && jj < a.kv_block && col < a.S && mask_visible(a.mask, p, col);
-                count += __popcll(__ballot(vis));
-            }
-        }
-        if (lane == 0)
-            tile_class[kb] = count == 0 ? TILE_EMPTY : (count == cells ? TILE_FULL : TILE_PARTIAL);
-    }
+    const int64_t row_id = (int64_t)bh * a.nQB + qb;
+    for (int kb = threadIdx.x; kb < a.nKB; kb += kCompactThreads)
+        tile_class[kb] = (uint8_t)a.kv_idx[row_id * a.nKB + kb];
     __syncthreads();
-
-    // Phase 2: wave 0 writes the partial list, wave 1 the full list.
     if (wave > 1) return;
+
+    // wave 0 writes the partial list, wave 1 the full list
     const uint8_t want = wave == 0 ? TILE_PARTIAL : TILE_FULL;
-    const int64_t row_id = ((int64_t)b * a.Hm + h) * a.nQB + qb;
     int* idx = (wave == 0 ? a.kv_idx : a.full_idx) + row_id * a.nKB;
     int* num = (wave == 0 ? a.kv_num : a.full_num) + row_id;
-
     int total = 0;
     for (int c0 = 0; c0 < a.nKB; c0 += 64) {
         const int kb = c0 + lane;
@@ -81,11 +118,26 @@ __global__ __launch_bounds__(kBuildThreads) void blockmask_build_kernel(BuildArg
     if (lane == 0) *num = total;
 }
 
+template <int KIND>
+hipError_t launch_classify(const BuildArgs& a, hipStream_t stream) {
+    dim3 grid((a.nKB + kClassifyWaves - 1) / kClassifyWaves, a.nQB, a.Bm * a.Hm);
+    hipLaunchKernelGGL(blockmask_classify<KIND>, grid, dim3(kClassifyWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream) {
-    dim3 grid(a.nQB, a.Hm, a.Bm);
-    hipLaunchKernelGGL(blockmask_build_kernel, grid, dim3(kBuildThreads), (size_t)a.nKB, stream, a);
+    hipError_t e;
+    switch (a.mask.kind) {
+    case MASK_NOOP: e = launch_classify<MASK_NOOP>(a, stream); break;
+    case MASK_CAUSAL: e = launch_classify<MASK_CAUSAL>(a, stream); break;
+    case MASK_CAUSAL_WINDOW_SINKS: e = launch_classify<MASK_CAUSAL_WINDOW_SINKS>(a, stream); break;
+    default: e = launch_classify<MASK_DOC_CAUSAL>(a, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    dim3 grid(a.nQB, a.Bm * a.Hm);
+    hipLaunchKernelGGL(blockmask_compact, grid, dim3(kCompactThreads), (size_t)a.nKB, stream, a);
     return hipGetLastError();
 }
 

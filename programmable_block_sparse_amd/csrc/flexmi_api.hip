@@ -124,6 +124,9 @@ flex_status flex_blockmask_build(const flex_mask_params* mask, int64_t L, int64_
     if (flex_status s = check_bm_dims(bm, L, S)) return s;
     if (bm->num_kv_blocks > 65536)
         return fail(FLEX_ERR_UNSUPPORTED, "at most 65536 KV blocks per row (got %d)", bm->num_kv_blocks);
+    if (bm->num_q_blocks > 65535 || (int64_t)bm->B * bm->H > 65535)
+        return fail(FLEX_ERR_UNSUPPORTED, "at most 65535 Q blocks and 65535 (B x H) mask rows (got %d, %d x %d)",
+                    bm->num_q_blocks, bm->B, bm->H);
     if (flex_status s = check_mask(mask, L, S)) return s;
 
     BuildArgs a;
@@ -175,6 +178,12 @@ static flex_status check_fwd(const void* q, const void* k, const void* v, int32_
     for (int i = 0; i < 3; ++i)
         if (qs[i] % chunk || ks[i] % chunk || vs[i] % chunk || qs[i] < 0 || ks[i] < 0 || vs[i] < 0)
             return fail(FLEX_ERR_LAYOUT, "strides must be non-negative multiples of %lld elements", (long long)chunk);
+    const int64_t elem = dtype == FLEX_BF16 ? 2 : 4;
+    if (ks[2] * elem * 64 >= (int64_t(1) << 31) || vs[2] * elem * 64 >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_UNSUPPORTED, "K/V row strides above 2^25 bytes are not supported");
+    if (S * std::max(ks[2], (int64_t)D) * elem >= (int64_t(1) << 31) ||
+        S * std::max(vs[2], (int64_t)D) * elem >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_UNSUPPORTED, "one K or V head slice (S x row stride) must stay below 2 GiB");
     if (score->kind < FLEX_SCORE_NONE || score->kind > FLEX_SCORE_SOFTCAP_ALIBI)
         return fail(FLEX_ERR_PARAM, "unknown score kind %d", score->kind);
     if (score->kind != FLEX_SCORE_NONE && !(score->cap > 0.0f && std::isfinite(score->cap)))
@@ -238,11 +247,30 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
     a.nKB = bm->num_kv_blocks;
     a.q_block = bm->q_block;
     a.kv_block = bm->kv_block;
+    // Fixed softmax reference when the soft-cap bounds every visible score:
+    // g < cap always, and a distance bias alpha*(kv - q) <= 0 under causal-type
+    // masks; rows then always keep their own (bias 0) key when q_offset + L <= S,
+    // so the range [ref - 120, ref + 64] (base 2) loses nothing.
+    a.ref_mode = 0;
+    a.ref_fixed = 0.0f;
+    if (dtype == FLEX_BF16 && score->kind != FLEX_SCORE_NONE) {
+        const double c2 = (double)score->cap * 1.4426950408889634;
+        bool ok = c2 <= 92.0;
+        if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI)
+            ok = ok && mask->kind != FLEX_MASK_NOOP && mask->q_offset + L <= S;
+        if (ok) {
+            a.ref_mode = 1;
+            a.ref_fixed = (float)(c2 <= 63.0 ? c2 : 120.0 - c2);
+        }
+    }
+    a.ksplit = prefill_ksplit(dtype, B, Hq, bm->num_q_blocks, bm->q_block, D);
+    a.splits = decode_splits(dtype, B, Hq, Hkv, (int)L, D, bm->q_block, bm->kv_block, bm->num_kv_blocks, bm->H);
     a.ws_acc = nullptr;
     a.ws_ml = nullptr;
-    a.splits = 1;
-    if (need > 0) {
+    if (a.splits > 0) {
+        const size_t rows = (size_t)a.splits * B * Hq * L;
         a.ws_acc = reinterpret_cast<float*>(workspace);
+        a.ws_ml = a.ws_acc + rows * D;
     }
     (void)hipGetLastError();
     hipError_t e = launch_attn_fwd(dtype, D, a, as_stream(stream));

@@ -47,11 +47,24 @@ struct FwdArgs {
     const int* full_num;
     const int* full_idx;
     int Bm, Hm, nQB, nKB, q_block, kv_block;
-    // split-KV decode
+    // softmax reference: 0 = running (moved lazily), 1 = fixed at ref_fixed
+    // (base 2), used when the soft-cap bounds every visible score
+    int ref_mode;
+    float ref_fixed;
+    // prefill row layout: 1 = 64-row workgroups, key halves split across waves
+    int ksplit;
+    // split-KV decode (splits == 0: prefill kernel)
     float* ws_acc;      // [splits][B][Hq][L][D] partial numerators
-    float* ws_ml;       // [splits][B][Hq][L][2]  partial (reference, denominator)
+    float* ws_ml;       // [splits][B][Hq][L][4]  partial (base-2 reference, sum p, sum rounded p, 0)
     int splits;
 };
+
+// Prefill row layout for these sizes (see attn_fwd.hip): 1 = key-split.
+int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D);
+
+// Number of key-range splits of the GQA-packed decode kernel for these sizes,
+// or 0 when the prefill kernel is used.
+int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, int kv_block, int nKB, int Hm);
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for an unsupported
 // combination (the host validated the combination before).

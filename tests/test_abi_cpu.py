@@ -104,6 +104,8 @@ def test_builder_rejects(lib):
     assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S, q_offset=5), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask(q_offset=1 << 30), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask(), 64, 64 * 70000, _bm(64, 64 * 70000, 64, 64)) == UNSUPPORTED
+    assert build(lib, _mask(), 70000, 64, _bm(70000, 64, 1, 64)) == UNSUPPORTED
+    assert build(lib, _mask(), 64, 64, _bm(64, 64, 64, 64, B=300, H=300)) == UNSUPPORTED
 
 
 class Fwd:
