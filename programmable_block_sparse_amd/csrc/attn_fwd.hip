@@ -53,12 +53,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
-// tanh(y) ~= y * (kTanh0 + kTanh1*y^2 + kTanh2*y^4) for |y| <= kTanhRange,
-// max abs error 1.3e-6 (weighted least-squares fit of the odd polynomial).
+// Soft-cap polynomials (iteratively reweighted least-squares fits of odd
+// polynomials, max abs error over the range evaluated in fp32):
+//   tanh(y) ~= y * (kTanh0 + kTanh1*y^2 + kTanh2*y^4) for |y| <= kTanhRange, 1.3e-6
+//   tanh(y) ~= y * (kLin0 + kLin1*y^2)                 for |y| <= kLinRange,  7.9e-6
+// The cubic is used only when cap * 7.9e-6 stays below kPolyScoreErr, a quarter
+// of the 1e-3 lse tolerance, i.e. for caps up to about 31.
 constexpr double kTanhRange = 0.4;
-constexpr double kTanh0 = 0.9999788900552721;
-constexpr double kTanh1 = -0.33225612213440997;
-constexpr double kTanh2 = 0.1194351036449146;
+constexpr double kTanh0 = 0.9999788560769031;
+constexpr double kTanh1 = -0.3322550629897203;
+constexpr double kTanh2 = 0.11942884091924301;
+constexpr double kLinRange = 0.25;
+constexpr double kLin0 = 0.9998436637524046;
+constexpr double kLin1 = -0.32320621727400445;
+constexpr double kLinErr = 7.9e-6;
+constexpr double kPolyScoreErr = 2.5e-4;
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -107,8 +116,10 @@ template <typename T> struct Precise { static constexpr bool value = sizeof(T) =
 struct TileConsts {
     float mul;        // NONE: scale*log2e; soft-cap exact path: 2*scale*log2e/cap
     float c2;         // cap*log2e
-    float k0, k1, k2; // polynomial path: g2 = acc*(k0 + k1*w + k2*w^2), w = acc^2
-    float amax;       // polynomial valid while |acc| <= amax
+    float k0, k1, k2; // quintic path: g2 = acc*(k0 + k1*w + k2*w^2), w = acc^2
+    float amax;       // quintic valid while |acc| <= amax
+    float j0, j1;     // cubic path: g2 = acc*(j0 + j1*w)
+    float amax1;      // cubic valid while |acc| <= amax1 (0 when the cap is too large)
     float alpha2;     // distance-bias slope * log2e of this lane's query head
     float ref_fixed;  // fixed base-2 reference
     double scale_d, cap_d, alpha_d;
@@ -126,6 +137,9 @@ __device__ __forceinline__ TileConsts make_consts(const FwdArgs& a, int hq) {
     c.k1 = (float)(scale * l2e * kTanh1 * r * r);
     c.k2 = (float)(scale * l2e * kTanh2 * r * r * r * r);
     c.amax = (float)(kTanhRange / r);
+    c.j0 = (float)(scale * l2e * kLin0);
+    c.j1 = (float)(scale * l2e * kLin1 * r * r);
+    c.amax1 = cap * kLinErr <= kPolyScoreErr ? (float)(kLinRange / r) : 0.0f;
     c.alpha_d = 0.0;
     c.alpha2 = 0.0f;
     if (a.score_kind == SCORE_SOFTCAP_ALIBI) {
@@ -477,9 +491,19 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
             float amax = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(s[r]));
-            // polynomial tanh, or the exact form cap - 2*cap / (1 + e^{2y}) when any
-            // score of the half is out of the polynomial's range (wave-uniform)
-            if (!__any(amax > tc.amax)) {
+            // polynomial tanh (cubic or quintic), or the exact form
+            // cap - 2*cap / (1 + e^{2y}) when a score of the half is out of the
+            // polynomials' range (wave-uniform choice)
+            if (!__any(amax > tc.amax1)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = base;
+                    if constexpr (SCORE == SCORE_SOFTCAP_ALIBI) x = __builtin_fmaf(tc.alpha2, (float)acc_row(r, 0), base);
+                    const float acc = s[r];
+                    const float poly = __builtin_fmaf(acc * acc, tc.j1, tc.j0);
+                    z[r] = __builtin_fmaf(acc, poly, x);
+                }
+            } else if (!__any(amax > tc.amax)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float x = base;

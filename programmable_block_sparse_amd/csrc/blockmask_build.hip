@@ -8,14 +8,18 @@
 // section: empty / full / partial tiles).  Unlike the eager path the blog's
 // cache section describes, no element-level dense mask is materialised.
 //
-// Two launches on the caller's stream:
-//   classify  one wave per tile; each lane owns a key column and the wave
-//             walks the tile's rows, so one v_cmp + ballot evaluates 64 cells
-//             and the visible-cell count accumulates in scalar registers.  The
-//             tile class (0 empty, 1 partial, 2 full) is parked in the tile's
-//             own kv_indices slot.
-//   compact   one workgroup per Q-block row reads the row's classes into LDS
-//             and rewrites kv_indices / full_kv_indices as ordered lists.
+// One launch, one workgroup per Q-block row:
+//   classify  waves take the row's tiles in turn.  Where the mask's rule is
+//             monotone in (q, kv) -- the causal part kv <= q, the window
+//             q - kv < W, the sink kv < sinks and the L/S bounds -- the class
+//             is read off the tile's corner cells, which gives exactly the
+//             class that counting would; otherwise each lane owns a key column
+//             and counts the visible cells of its column in closed form (the
+//             window and sinks bound an interval of rows; for documents the
+//             block's rows are cut into runs of equal id, so the count is a sum
+//             over the runs that carry the column's id), and a wave reduction
+//             gives the tile count.  Classes go to LDS, two bits per tile.
+//   compact   wave 0 writes the ordered partial list, wave 1 the full list.
 //
 // Layout conventions: cells beyond L or S are not visible; each index row
 // lists its tiles ascending, then the remaining tile indices ascending.
@@ -25,89 +29,190 @@ namespace flexmi {
 
 namespace {
 
-constexpr int kClassifyWaves = 8;
-constexpr int kCompactThreads = 256;
+constexpr int kMaxQBlock = 1024;
 
-enum : int { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
+enum : int { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2, TILE_COUNT = 3 };
 
-// Ballot of the visible cells of one query position p over this lane's key
-// column (branch-free within the row; col_ok folds the tile and S bounds).
+// Class of a tile decided from its corners, or TILE_COUNT when the cells have
+// to be counted.  Rows [r0, r1] (logical positions p0 = r0 + off, p1), columns
+// [c0, c1], all clipped to L and S; `clipped` tells whether the tile extends
+// past L or S (then it cannot be full).
 template <int KIND>
-__device__ __forceinline__ uint64_t row_ballot(const MaskArgs& m, int p, int col, bool col_ok, int doc_p,
-                                               int doc_col) {
-    bool v;
+__device__ __forceinline__ int corner_class(const MaskArgs& m, int p0, int p1, int c0, int c1, bool clipped) {
     if constexpr (KIND == MASK_NOOP) {
-        v = col_ok;
-    } else if constexpr (KIND == MASK_CAUSAL) {
-        v = col_ok & (col <= p);
-    } else if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS) {
-        v = col_ok & (col <= p) & ((p - col < m.window) | (col < m.sinks));
+        return clipped ? TILE_PARTIAL : TILE_FULL;
     } else {
-        v = col_ok & (col <= p) & (doc_p == doc_col);
+        if (c0 > p1) return TILE_EMPTY;                       // every kv > every q: causal part fails
+        if constexpr (KIND == MASK_CAUSAL) {
+            if (c1 <= p0) return clipped ? TILE_PARTIAL : TILE_FULL;
+            return TILE_PARTIAL;                              // both visible and hidden cells exist
+        } else if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS) {
+            // hidden everywhere: beyond the window for every cell and past the sinks
+            if (p0 - c1 >= m.window && c0 >= m.sinks) return TILE_EMPTY;
+            // visible everywhere: causal for every cell and inside the window or a sink
+            if (c1 <= p0 && (p1 - c0 < m.window || c1 < m.sinks)) return clipped ? TILE_PARTIAL : TILE_FULL;
+            return TILE_COUNT;
+        } else {
+            return TILE_COUNT;                                // document ids have to be compared
+        }
     }
-    return __ballot(v);
 }
 
+// Document id of a position, or `none` outside the id array (such positions
+// belong to no document).
+__device__ __forceinline__ int doc_at(const MaskArgs& m, int p, int none) {
+    return (p >= 0 && p < m.doc_len) ? __ldg(m.doc_id + p) : none;
+}
+
+__device__ __forceinline__ int class_of(const uint32_t* words, int kb) {
+    return (int)((words[kb >> 4] >> (2 * (kb & 15))) & 3u);
+}
+
+// Masks that count cells use 16 waves; the others only need the two that
+// write the lists.
 template <int KIND>
-__global__ __launch_bounds__(kClassifyWaves * 64) void blockmask_classify(BuildArgs a) {
+constexpr int build_threads() {
+    return (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL) ? 1024 : 128;
+}
+constexpr int kCountBatch = 8;
+
+template <int KIND>
+__global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildArgs a) {
+    constexpr int kBuildThreads = build_threads<KIND>();
+    constexpr int kBuildWaves = kBuildThreads / 64;
+    // Document runs of this block's rows: maximal stretches of equal id.
+    __shared__ int run_start[kMaxQBlock + 1];
+    __shared__ int run_doc[kMaxQBlock];
+    __shared__ int run_count;
+    extern __shared__ uint32_t tile_class[];  // 2 bits per tile, 16 tiles per word
     const int lane = threadIdx.x & 63;
-    const int kb = blockIdx.x * kClassifyWaves + (threadIdx.x >> 6);
-    if (kb >= a.nKB) return;
-    const int qb = blockIdx.y;
-    const int bh = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int qb = blockIdx.x;
+    const int bh = blockIdx.y;
     const int row0 = qb * a.q_block;
     const int rows = min(a.q_block, a.L - row0);
     const int64_t row_id = (int64_t)bh * a.nQB + qb;
-    int64_t count = 0;
-    for (int j0 = 0; j0 < a.kv_block; j0 += 64) {
-        const int jj = j0 + lane;
-        const int col = kb * a.kv_block + jj;
-        const bool col_ok = (jj < a.kv_block) & (col < a.S);
-        int doc_col = -1;
-        if constexpr (KIND == MASK_DOC_CAUSAL)
-            doc_col = (col_ok && col < a.mask.doc_len) ? __ldg(a.mask.doc_id + col) : -1;
-        for (int i = 0; i < rows; ++i) {
-            const int p = row0 + i + a.mask.q_offset;
-            int doc_p = -2;
-            if constexpr (KIND == MASK_DOC_CAUSAL)
-                doc_p = (p >= 0 && p < a.mask.doc_len) ? __ldg(a.mask.doc_id + p) : -2;
-            count += __popcll(row_ballot<KIND>(a.mask, p, col, col_ok, doc_p, doc_col));
+    const int p0 = row0 + a.mask.q_offset, p1 = p0 + rows - 1;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if constexpr (KIND == MASK_DOC_CAUSAL) {
+        if (wave == 0) {
+            int runs = 0;
+            for (int i0 = 0; i0 < rows; i0 += 64) {
+                const int i = i0 + lane;
+                const int d = i < rows ? doc_at(a.mask, p0 + i, -2) : 0;
+                const int prev = (i > 0 && i < rows) ? doc_at(a.mask, p0 + i - 1, -2) : 0;
+                const bool start = i < rows && (i == 0 || d != prev);
+                const uint64_t starts = __ballot(start);
+                if (start) {
+                    const int r = runs + __popcll(starts & below);
+                    run_start[r] = i;
+                    run_doc[r] = d;
+                }
+                runs += __popcll(starts);
+            }
+            if (lane == 0) {
+                run_start[runs] = rows;
+                run_count = runs;
+            }
         }
     }
-    if (lane == 0) {
-        const int64_t cells = (int64_t)a.q_block * a.kv_block;
-        a.kv_idx[row_id * a.nKB + kb] = count == 0 ? TILE_EMPTY : (count == cells ? TILE_FULL : TILE_PARTIAL);
-    }
-}
 
-__global__ __launch_bounds__(kCompactThreads) void blockmask_compact(BuildArgs a) {
-    extern __shared__ uint8_t tile_class[];  // [nKB]
-    const int qb = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t row_id = (int64_t)bh * a.nQB + qb;
-    for (int kb = threadIdx.x; kb < a.nKB; kb += kCompactThreads)
-        tile_class[kb] = (uint8_t)a.kv_idx[row_id * a.nKB + kb];
+    // Phase 1: classify.  Corner rules first (sixteen tiles per thread), then
+    // the tiles that need counting, one per wave.
+    const int words = (a.nKB + 15) >> 4;
+    for (int w = threadIdx.x; w < words; w += kBuildThreads) {
+        uint32_t word = 0;
+        for (int t = 0; t < 16; ++t) {
+            const int kb = w * 16 + t;
+            if (kb >= a.nKB) break;
+            const int c0 = kb * a.kv_block;
+            const int c1 = min(c0 + a.kv_block, a.S) - 1;
+            const bool clipped = rows < a.q_block || c0 + a.kv_block > a.S;
+            word |= (uint32_t)corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped) << (2 * t);
+        }
+        tile_class[w] = word;
+    }
     __syncthreads();
+    if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL) {
+        // A wave takes kCountBatch of its tiles at a time so that the column id
+        // loads of the batch are in flight together.
+        const int runs = KIND == MASK_DOC_CAUSAL ? run_count : 0;
+        for (int kb0 = wave; kb0 < a.nKB; kb0 += kBuildWaves * kCountBatch) {
+            bool todo[kCountBatch];
+            bool any = false;
+#pragma unroll
+            for (int u = 0; u < kCountBatch; ++u) {
+                const int kb = kb0 + u * kBuildWaves;
+                todo[u] = kb < a.nKB && class_of(tile_class, kb) == TILE_COUNT;   // wave-uniform
+                any |= todo[u];
+            }
+            if (!any) continue;
+            int count[kCountBatch];   // visible cells of this lane's columns, per tile
+#pragma unroll
+            for (int u = 0; u < kCountBatch; ++u) count[u] = 0;
+            for (int j0 = 0; j0 < a.kv_block; j0 += 64) {
+                const int jj = j0 + lane;
+                int doc_col[kCountBatch];
+                if constexpr (KIND == MASK_DOC_CAUSAL) {
+#pragma unroll
+                    for (int u = 0; u < kCountBatch; ++u) {
+                        const int col = (kb0 + u * kBuildWaves) * a.kv_block + jj;
+                        doc_col[u] = (todo[u] && jj < a.kv_block && col < a.S) ? doc_at(a.mask, col, -1) : -1;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kCountBatch; ++u) {
+                    const int col = (kb0 + u * kBuildWaves) * a.kv_block + jj;
+                    if (!todo[u] || jj >= a.kv_block || col >= a.S) continue;
+                    // rows of this column that pass the causal part: p in [max(p0, col), p1]
+                    const int lo = max(p0, col);
+                    if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS) {
+                        // a sink column is seen by every later row; any other
+                        // column by rows p < col + window
+                        const int hi = (col < a.mask.sinks || a.mask.window > p1 - col) ? p1 : col + a.mask.window - 1;
+                        count[u] += max(0, hi - lo + 1);
+                    } else {
+                        // rows of a run with the column's document, at or after the column
+                        for (int r = 0; r < runs; ++r) {
+                            if (run_doc[r] != doc_col[u]) continue;
+                            const int s0 = max(p0 + run_start[r], lo);
+                            count[u] += max(0, p0 + run_start[r + 1] - s0);
+                        }
+                    }
+                }
+            }
+            const int cells = a.q_block * a.kv_block;
+#pragma unroll
+            for (int u = 0; u < kCountBatch; ++u) {
+                if (!todo[u]) continue;
+                int c = count[u];
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+                const int kb = kb0 + u * kBuildWaves;
+                const uint32_t cls = c == 0 ? TILE_EMPTY : (c == cells ? TILE_FULL : TILE_PARTIAL);
+                // the tile's two bits read TILE_COUNT (both set): clear the ones cls lacks
+                if (lane == 0) atomicAnd(&tile_class[kb >> 4], ~((TILE_COUNT & ~cls) << (2 * (kb & 15))));
+            }
+        }
+        __syncthreads();
+    }
     if (wave > 1) return;
 
-    // wave 0 writes the partial list, wave 1 the full list
-    const uint8_t want = wave == 0 ? TILE_PARTIAL : TILE_FULL;
+    // Phase 2: wave 0 writes the partial list, wave 1 the full list.
+    const int want = wave == 0 ? TILE_PARTIAL : TILE_FULL;
     int* idx = (wave == 0 ? a.kv_idx : a.full_idx) + row_id * a.nKB;
     int* num = (wave == 0 ? a.kv_num : a.full_num) + row_id;
     int total = 0;
     for (int c0 = 0; c0 < a.nKB; c0 += 64) {
         const int kb = c0 + lane;
-        total += __popcll(__ballot(kb < a.nKB && tile_class[kb] == want));
+        total += __popcll(__ballot(kb < a.nKB && class_of(tile_class, kb) == want));
     }
     int hits = 0;    // listed tiles before this chunk
     int misses = 0;  // other tiles before this chunk
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int c0 = 0; c0 < a.nKB; c0 += 64) {
         const int kb = c0 + lane;
         const bool in = kb < a.nKB;
-        const bool hit = in && tile_class[kb] == want;
+        const bool hit = in && class_of(tile_class, kb) == want;
         const uint64_t hit_mask = __ballot(hit);
         const uint64_t miss_mask = __ballot(in && !hit);
         if (hit) idx[hits + __popcll(hit_mask & below)] = kb;
@@ -119,26 +224,22 @@ __global__ __launch_bounds__(kCompactThreads) void blockmask_compact(BuildArgs a
 }
 
 template <int KIND>
-hipError_t launch_classify(const BuildArgs& a, hipStream_t stream) {
-    dim3 grid((a.nKB + kClassifyWaves - 1) / kClassifyWaves, a.nQB, a.Bm * a.Hm);
-    hipLaunchKernelGGL(blockmask_classify<KIND>, grid, dim3(kClassifyWaves * 64), 0, stream, a);
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream) {
+    dim3 grid(a.nQB, a.Bm * a.Hm);
+    const size_t lds = (size_t)((a.nKB + 15) >> 4) * sizeof(uint32_t);
+    hipLaunchKernelGGL(blockmask_build<KIND>, grid, dim3(build_threads<KIND>()), lds, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream) {
-    hipError_t e;
     switch (a.mask.kind) {
-    case MASK_NOOP: e = launch_classify<MASK_NOOP>(a, stream); break;
-    case MASK_CAUSAL: e = launch_classify<MASK_CAUSAL>(a, stream); break;
-    case MASK_CAUSAL_WINDOW_SINKS: e = launch_classify<MASK_CAUSAL_WINDOW_SINKS>(a, stream); break;
-    default: e = launch_classify<MASK_DOC_CAUSAL>(a, stream); break;
+    case MASK_NOOP: return launch_build<MASK_NOOP>(a, stream);
+    case MASK_CAUSAL: return launch_build<MASK_CAUSAL>(a, stream);
+    case MASK_CAUSAL_WINDOW_SINKS: return launch_build<MASK_CAUSAL_WINDOW_SINKS>(a, stream);
+    default: return launch_build<MASK_DOC_CAUSAL>(a, stream);
     }
-    if (e != hipSuccess) return e;
-    dim3 grid(a.nQB, a.Bm * a.Hm);
-    hipLaunchKernelGGL(blockmask_compact, grid, dim3(kCompactThreads), (size_t)a.nKB, stream, a);
-    return hipGetLastError();
 }
 
 }  // namespace flexmi

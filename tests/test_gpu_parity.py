@@ -67,6 +67,40 @@ def test_blockmask_fuzz_bit_exact(dev):
     assert n_cases > 300
 
 
+def test_blockmask_extreme_parameters(dev):
+    """Windows up to INT32_MAX, sinks past S, 1024-wide tiles and document ids
+    that are not sorted (a run of equal ids per cell, or ids repeating far
+    apart), all against the oracle's cell-by-cell count."""
+    rng = np.random.default_rng(99)
+    cases = []
+    for window in (1, 2, 1000, 2**31 - 1):
+        for sinks in (0, 1, 5000):
+            cases.append(("causal_window_sinks", window, sinks, None))
+    for pattern in ("alternating", "random3", "reversed_runs"):
+        cases.append(("doc_causal", 0, 0, pattern))
+    n = 0
+    for kind, window, sinks, pattern in cases:
+        for L, S, QB, KB, off in ((1500, 2100, 1024, 1024, 600), (700, 700, 128, 64, 0), (33, 2000, 16, 1000, 1967)):
+            doc_np = doc_t = None
+            if kind == "doc_causal":
+                m = max(S, off + L)
+                if pattern == "alternating":
+                    doc_np = (np.arange(m) % 2).astype(np.int32)
+                elif pattern == "random3":
+                    doc_np = rng.integers(0, 3, size=m).astype(np.int32)
+                else:
+                    doc_np = _rand_doc(rng, m)[::-1].copy()
+                doc_t = torch.from_numpy(doc_np).to(dev)
+            spec, mod = _mask_pair(kind, window, sinks, off, doc_np, doc_t)
+            print(f"[blockmask] {kind} window={window} sinks={sinks} doc={pattern} L={L} S={S} "
+                  f"tiles={QB}x{KB} q_offset={off}", flush=True)
+            gpu = pbs.flex_blockmask_build(spec, L, S, QB, KB, device=dev)
+            ref = build_block_mask(mod, L, S, QB, KB, q_offset=off)
+            assert_block_mask_equal(gpu, ref)
+            n += 1
+    assert n == 45
+
+
 @pytest.mark.parametrize("name", WORKLOAD_ORDER)
 def test_blockmask_workloads_bit_exact(dev, name):
     w = WORKLOADS[name]
@@ -174,6 +208,27 @@ def test_attention_large_scores_and_values(dev):
              score=dict(kind="softcap", cap=50.0), mask_kind="noop", scale=2.0, what="scale 2 bf16")
     run_case(dev, seed=10, dtype="bf16", B=1, Hq=2, Hkv=2, L=256, S=256, D=128, qb=128, kb=64,
              score=dict(kind="none"), mask_kind="causal", value_scale=0.5, what="values")
+
+
+@pytest.mark.parametrize("mask_kind", ["causal", "noop"])
+@pytest.mark.parametrize("score", [dict(kind="softcap", cap=30.0), dict(kind="softcap_alibi", cap=30.0),
+                                   dict(kind="softcap", cap=50.0)])
+def test_softcap_tiers_by_score_magnitude(dev, mask_kind, score):
+    """Rows scaled so that different waves take the cubic, quintic and exact tanh paths."""
+    rng = np.random.default_rng(21)
+    B, H, L, S, D = 1, 2, 256, 256, 64
+    q = rng.standard_normal((B, H, L, D), dtype=np.float32)
+    q *= np.repeat(np.array([0.3, 1.0, 2.5, 6.0], dtype=np.float32), L // 4)[None, None, :, None]
+    k = rng.standard_normal((B, H, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, S, D), dtype=np.float32)
+    mspec, mmod = _mask_pair(mask_kind, q_offset=0)
+    bm = pbs.flex_blockmask_build(mspec, L, S, 128, 64, device=dev)
+    out, lse = pbs.flex_attn_fwd(_tensor(q, "bf16", dev), _tensor(k, "bf16", dev), _tensor(v, "bf16", dev),
+                                 block_mask=bm, score=pbs.ScoreSpec(**score), mask=mspec)
+    torch.cuda.synchronize()
+    out_ref, lse_ref = attention(_widen(q, "bf16"), _widen(k, "bf16"), _widen(v, "bf16"), scale=pbs.default_scale(D),
+                                 score=ScoreMod(**score), mask=mmod, q_offset=0)
+    assert_attention_close(out, lse, out_ref, lse_ref, "bf16", f"tiers {score} {mask_kind}")
 
 
 def test_lse_optional_and_strided_inputs(dev):
