@@ -40,7 +40,61 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")
     return p.parse_args()
+
+
+# Kernel sources whose code the HBM traffic figures under profiles/ were taken
+# on; a figure is reported only while these files are unchanged.
+KERNEL_SOURCES = ("programmable_block_sparse_amd/csrc/attn_fwd.hip",
+                  "programmable_block_sparse_amd/csrc/device_common.hpp",
+                  "programmable_block_sparse_amd/csrc/internal.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per forward launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    """Device-to-device copies of a known size: what FETCH_SIZE and WRITE_SIZE
+    read for them scales the counters of the attention kernels to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: copy {i} of {mib} MiB done", file=sys.stderr, flush=True)
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def visited_flops_per_head(bm_np, w):
@@ -63,6 +117,10 @@ def main():
         print("bench.py: multi-GPU runs are not part of this build (one GPU per box); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import programmable_block_sparse_amd as pbs
@@ -160,7 +218,7 @@ def main():
         peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "attn_fwd_decode + attn_fwd_combine" if ws_bytes else "attn_fwd_prefill"
     roof["algorithmic_per_launch"] = flops if roof["unit"] == "TFLOP/s" else alg_bytes
 

@@ -82,12 +82,14 @@ template <> struct Elem<__bf16> {
 };
 
 // LDS geometry of one pipeline buffer: K[key][d], V, doc ids[key].  bf16 keeps
-// V row-major (V[key][d]) and reads the PV operand with ds_read_b64_tr_b16;
-// fp32 stores V^T[d][key].
+// K and V row-major and unpadded, filled by LDS-DMA buffer loads, with the
+// 16-byte chunks of each row permuted (swz below) so that neither the K
+// operand reads nor the ds_read_b64_tr_b16 V reads collide in LDS banks; fp32
+// stages through registers into padded K[key][d] and V^T[d][key].
 template <typename T, int D> struct Tiles {
     static constexpr bool kVRowMajor = sizeof(T) == 2;
-    static constexpr int kStrideK = D + Elem<T>::kPadK;
-    static constexpr int kStrideV = kVRowMajor ? D + Elem<T>::kPadK : kTileN + Elem<T>::kPadV;
+    static constexpr int kStrideK = sizeof(T) == 2 ? D : D + Elem<T>::kPadK;
+    static constexpr int kStrideV = kVRowMajor ? D : kTileN + Elem<T>::kPadV;
     static constexpr int kElemsK = kTileN * kStrideK;
     static constexpr int kElemsV = kVRowMajor ? kTileN * kStrideV : D * kStrideV;
     static constexpr int kDocOffset = (kElemsK + kElemsV) * (int)sizeof(T);   // bytes
@@ -252,6 +254,73 @@ __device__ __forceinline__ void stage_store(const Stage<T, D>& st, char* __restr
     if (with_doc && tid < kTileN) reinterpret_cast<int*>(buf + G::kDocOffset)[tid] = st.doc;
 }
 
+// bf16 tiles: 16-byte chunk c of LDS row r (a key) holds the row's chunk
+// c ^ swz(r).  swz depends on r mod 16 only, so row offsets that are
+// multiples of 16 stay immediate offsets.  Both patterns were checked for
+// 32 and 64 LDS banks against the two read shapes: eight or sixteen lanes
+// reading one chunk of consecutive rows (K operand, ds_read_b128) and four
+// consecutive rows x two or four chunks (V, ds_read_b64_tr_b16).
+template <int D> __device__ __forceinline__ constexpr int swz(int r) {
+    return D == 64 ? ((2 * (r & 15) + ((r & 15) >> 2)) & 7) : ((5 * r) & 15);
+}
+
+// Per-lane LDS byte offsets of the bf16 operand reads within a buffer (fixed
+// per lane): K operand step s of key block kb2_base (add 32 rows per further
+// block), and V chunk pairs for dims 32*db.. at rows 4*hf + j/4 (+8 for hi) of
+// the first 16-row group of that block.
+template <typename T, int D> struct LdsAddr {};
+template <int D> struct LdsAddr<__bf16, D> {
+    int k[D / 16];
+    int v[D / 32][2];
+};
+
+template <int D> __device__ __forceinline__ LdsAddr<__bf16, D> lds_addr_bf16(int lane, int kb2_base) {
+    constexpr int kRowBytes = 2 * D, kChunkMask = D / 8 - 1;
+    LdsAddr<__bf16, D> la;
+    const int hf = lane >> 5, r = lane & 31;
+    const int g = hf ^ swz<D>(r);
+    const int blk = kb2_base * 32 * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) la.k[s] = blk + r * kRowBytes + (((2 * s) ^ g) & kChunkMask) * 16;
+    const int j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * hf + (j >> 2) + 8 * h;
+            const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+            la.v[db][h] = blk + row * kRowBytes + ((c ^ swz<D>(row)) & kChunkMask) * 16 + (j & 1) * 8;
+        }
+    return la;
+}
+
+// LDS-DMA fill of one bf16 tile: wave w's instruction i writes the 64
+// contiguous chunks (i*4 + w)*64 .. +63 of the K (then V) area, lane l the
+// chunk at position l; the lane loads the global chunk that the swizzle puts
+// there.  Offsets are bytes within the tile's rows.
+template <int D> struct DmaPlan {
+    static constexpr int kInsts = D / 32;   // per wave, for K and again for V
+    int k[kInsts];
+    int v[kInsts];
+};
+
+template <int D>
+__device__ __forceinline__ DmaPlan<D> dma_plan(int k_row_bytes, int v_row_bytes, int wave, int lane) {
+    constexpr int kChunksPerRow = D / 8;
+    DmaPlan<D> pl;
+#pragma unroll
+    for (int i = 0; i < DmaPlan<D>::kInsts; ++i) {
+        const int pos = (i * 4 + wave) * 64 + lane;
+        const int row = pos / kChunksPerRow;
+        const int chunk = (pos % kChunksPerRow) ^ swz<D>(row);
+        pl.k[i] = row * k_row_bytes + chunk * 16;
+        pl.v[i] = row * v_row_bytes + chunk * 16;
+    }
+    return pl;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // Q operand (MFMA B operand, one query row per lane & 31).
 template <typename T, int D> struct QRegs;
 template <int D> struct QRegs<__bf16, D> {
@@ -285,18 +354,20 @@ __device__ __forceinline__ void load_q(QRegs<T, D>& qr, const T* __restrict__ qr
 
 // S^T block (32 keys x 32 queries) for keys [kb2*32, kb2*32+32) of the LDS tile.
 template <typename T, int D>
-__device__ __forceinline__ f32x16_t qk_block(const QRegs<T, D>& qr, const T* __restrict__ Ks, int kb2, int lane) {
+__device__ __forceinline__ f32x16_t qk_block(const QRegs<T, D>& qr, const char* __restrict__ buf,
+                                             const LdsAddr<T, D>& la, int kb2, int lane) {
     using G = Tiles<T, D>;
     const int hf = lane >> 5;
-    const T* krow = Ks + (kb2 * 32 + (lane & 31)) * G::kStrideK;
     f32x16_t acc = {};
     if constexpr (sizeof(T) == 2) {
+        const char* kblk = buf + kb2 * 32 * 2 * D;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + 16 * s + 8 * hf);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kblk + la.k[s]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr.x[s], acc, 0, 0, 0);
         }
     } else {
+        const T* krow = reinterpret_cast<const T*>(buf) + (kb2 * 32 + (lane & 31)) * G::kStrideK;
 #pragma unroll
         for (int s4 = 0; s4 < D / 8; ++s4) {
             const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(krow + hf * (D / 2) + 4 * s4);
@@ -338,23 +409,18 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 // row keybase + j/4, dims d0 + 4*(j%4), which hands lane j the four values
 // V[keybase + e][d0 + j], e = 0..3: the A-operand slots of V^T for the keys
 // whose probabilities the same lane holds in pb (keys 16t + 4hf + e and
-// 16t + 8 + 4hf + e, t = 2*kb2 + tt).
+// 16t + 8 + 4hf + e, t = 2*kb2 + tt).  The swizzled byte offsets of those
+// source addresses are in la.v.
 template <int D>
-__device__ __forceinline__ void pv_bf16(f32x16_t (&o)[D / 32], const bf16x8_t (&pb)[2], const __bf16* __restrict__ Vs,
-                                        int kb2, int lane) {
-    using G = Tiles<__bf16, D>;
-    const int hf = lane >> 5;
-    const int j = lane & 15;
-    const int src = (j >> 2) * G::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+__device__ __forceinline__ void pv_bf16(f32x16_t (&o)[D / 32], const bf16x8_t (&pb)[2], const char* __restrict__ Vs,
+                                        const LdsAddr<__bf16, D>& la, int kb2) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        const int t = 2 * kb2 + tt;
-        const __bf16* base_lo = Vs + (16 * t + 4 * hf) * G::kStrideV + src;
-        const __bf16* base_hi = base_lo + 8 * G::kStrideV;
+        const char* grp = Vs + (16 * (2 * kb2 + tt)) * 2 * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base_lo + 32 * db));
-            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base_hi + 32 * db));
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(grp + la.v[db][0]));
+            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(grp + la.v[db][1]));
             const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[tt], o[db], 0, 0, 0);
         }
@@ -455,19 +521,19 @@ __device__ __forceinline__ void apply_mask(float (&z)[16], const MaskArgs& m, in
 // every tile go to two different waves that own the same query rows; their
 // partial states are merged once at the end (merge_key_halves).
 template <typename T, int D, int SCORE, bool FIXED>
-__device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* __restrict__ buf, f32x16_t (&o)[D / 32],
+__device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* __restrict__ buf,
+                                             const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
                                              RowState<Precise<T>::value>& st, const TileConsts& tc,
                                              const MaskArgs& mask, bool masked, int kv0, int S, const LaneRow& row,
-                                             int kb2, int lane) {
+                                             int kb2, int kb2_lds, int lane) {
     using G = Tiles<T, D>;
     constexpr bool P = Precise<T>::value;
     using RefT = typename std::conditional<P, double, float>::type;
     const int hf = lane >> 5;
-    const T* Ks = reinterpret_cast<const T*>(buf);
-    const T* Vs = Ks + G::kElemsK;
+    const T* Vs = reinterpret_cast<const T*>(buf) + G::kElemsK;
     const int* doc_lds = reinterpret_cast<const int*>(buf + G::kDocOffset);
     {
-        const f32x16_t s = qk_block<T, D>(qr, Ks, kb2, lane);
+        const f32x16_t s = qk_block<T, D>(qr, buf, la, sizeof(T) == 2 ? kb2_lds : kb2, lane);
         float z[16];
         const RefT ref_sub = FIXED ? (RefT)tc.ref_fixed : ((st.ref == (RefT)kNegInf) ? (RefT)0 : st.ref);
         const int key_base = kv0 + 32 * kb2 + 4 * hf;
@@ -568,8 +634,98 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
             bf16x8_t pb[2];
             pack_p(pb, z);
             st.lr += sum_packed(pb);
-            pv_bf16<D>(o, pb, Vs, kb2, lane);
+            pv_bf16<D>(o, pb, reinterpret_cast<const char*>(Vs), la, kb2_lds);
         }
+    }
+}
+
+// bf16 tile walk: tiles arrive by LDS-DMA (no staging registers), double
+// buffered, with the loop unrolled over the two buffers so every LDS operand
+// address is a per-lane constant plus an immediate.
+template <int D, int SCORE, bool FIXED, bool KSPLIT>
+__device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* __restrict__ kbase,
+                                                const __bf16* __restrict__ vbase, const QRegs<__bf16, D>& qr,
+                                                const int* __restrict__ part_idx, int n_part,
+                                                const int* __restrict__ full_idx, int tile_lo, int tile_hi,
+                                                const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
+                                                f32x16_t (&o)[D / 32], RowState<false>& st, char* lds) {
+    using G = Tiles<__bf16, D>;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int sub_per_block = a.kv_block / kTileN;
+    const bool with_doc = a.mask.kind == MASK_DOC_CAUSAL;
+
+    auto tile_kv0 = [&](int t, bool& masked) -> int {
+        const int blk = sub_per_block == 1 ? t : t / sub_per_block;
+        const int sub = t - blk * sub_per_block;
+        int kb;
+        if (blk < n_part) { kb = part_idx[blk]; masked = true; }
+        else { kb = full_idx[blk - n_part]; masked = false; }
+        return kb * a.kv_block + sub * kTileN;
+    };
+
+    if (tile_lo >= tile_hi) return;
+    SliceRsrc sr;
+    sr.k_row_bytes = (int)(a.k_sr * (int64_t)sizeof(__bf16));
+    sr.v_row_bytes = (int)(a.v_sr * (int64_t)sizeof(__bf16));
+    sr.k = slice_rsrc(kbase, sr.k_row_bytes, a.S);
+    sr.v = slice_rsrc(vbase, sr.v_row_bytes, a.S);
+    sr.doc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
+    const DmaPlan<D> pl = dma_plan<D>(sr.k_row_bytes, sr.v_row_bytes, wave, lane);
+    // key-split waves read only their own key half: fold it into the offsets
+    const LdsAddr<__bf16, D> la = lds_addr_bf16<D>(lane, KSPLIT ? kh : 0);
+
+    auto issue = [&](char* buf, int kv0) {
+        const int ko = kv0 * sr.k_row_bytes, vo = kv0 * sr.v_row_bytes;
+#pragma unroll
+        for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.k, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
+                                                     ko, 0, 0);
+#pragma unroll
+        for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.v, (lds_void_t*)(buf + G::kElemsK * 2 + (i * 4 + wave) * 1024),
+                                                     16, pl.v[i], vo, 0, 0);
+        if (with_doc && wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.doc, (lds_void_t*)(buf + G::kDocOffset), 4, lane * 4, kv0 * 4,
+                                                     0, 0);
+    };
+    // DMA writes to LDS count on vmcnt: drain them before the barrier that
+    // publishes the buffer.
+    auto publish = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    bool masked;
+    int kv0 = tile_kv0(tile_lo, masked);
+    issue(lds, kv0);
+    publish();
+    auto step = [&](auto bufc, int t) {
+        constexpr int B = decltype(bufc)::value;
+        bool next_masked = false;
+        int next_kv0 = 0;
+        const bool has_next = t + 1 < tile_hi;
+        if (has_next) {
+            next_kv0 = tile_kv0(t + 1, next_masked);
+            issue(lds + (B ^ 1) * G::kBufBytes, next_kv0);
+        }
+        const char* cur = lds + B * G::kBufBytes;
+        if (wave_active) {
+            if constexpr (KSPLIT) {
+                process_tile<__bf16, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, kh, 0,
+                                                      lane);
+            } else {
+                process_tile<__bf16, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 0, 0, lane);
+                process_tile<__bf16, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 1, 1, lane);
+            }
+        }
+        publish();
+        kv0 = next_kv0;
+        masked = next_masked;
+    };
+    for (int t = tile_lo; t < tile_hi; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < tile_hi) step(std::integral_constant<int, 1>{}, t + 1);
     }
 }
 
@@ -582,7 +738,12 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
                                             const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                             const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
                                             f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds) {
+    if constexpr (sizeof(T) == 2) {
+        attend_rows_dma<D, SCORE, FIXED, KSPLIT>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo, tile_hi, tc,
+                                                 row, wave_active, kh, o, st, lds);
+    } else {
     using G = Tiles<T, D>;
+    const LdsAddr<T, D> la{};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int sub_per_block = a.kv_block / kTileN;
@@ -623,16 +784,17 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
         const char* cur = lds + buf * G::kBufBytes;
         if (wave_active) {
             if constexpr (KSPLIT) {
-                process_tile<T, D, SCORE, FIXED>(qr, cur, o, st, tc, a.mask, masked, kv0, a.S, row, kh, lane);
+                process_tile<T, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, kh, kh, lane);
             } else {
-                process_tile<T, D, SCORE, FIXED>(qr, cur, o, st, tc, a.mask, masked, kv0, a.S, row, 0, lane);
-                process_tile<T, D, SCORE, FIXED>(qr, cur, o, st, tc, a.mask, masked, kv0, a.S, row, 1, lane);
+                process_tile<T, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 0, 0, lane);
+                process_tile<T, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 1, 1, lane);
             }
         }
         if (has_next) stage_store<T, D>(stage, lds + (buf ^ 1) * G::kBufBytes, with_doc, tid);
         __syncthreads();
         kv0 = next_kv0;
         masked = next_masked;
+    }
     }
 }
 
@@ -746,7 +908,15 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D>::value)) void att
     const int qb = a.nQB - 1 - (int)(blockIdx.x / (BH * parts));
     const int rem = (int)(blockIdx.x % (BH * parts));
     const int part = rem / BH;
-    const int bh = rem % BH;
+    int bh = rem % BH;
+    // Workgroup i runs on XCD i % 8, each XCD with its own L2.  Under GQA the
+    // ids are permuted so that the `group` query heads of one K/V head land on
+    // the same XCD (and stay there for every Q block), so their K/V tiles are
+    // fetched into one L2 instead of `group`.
+    if (a.group > 1 && BH % (8 * a.group) == 0) {
+        const int xcd = bh & 7, k = bh >> 3;
+        bh = (xcd + 8 * (k / a.group)) * a.group + k % a.group;
+    }
     const int b = bh / a.Hq, hq = bh % a.Hq, hkv = hq / a.group;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
     const int rg = KSPLIT ? (wave & 1) : wave, kh = KSPLIT ? (wave >> 1) : 0;
