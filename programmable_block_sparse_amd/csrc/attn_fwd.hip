@@ -114,6 +114,9 @@ __device__ __forceinline__ float wave_half_sum(float x) {
 
 template <typename T> struct Precise { static constexpr bool value = sizeof(T) == 4; };
 
+// Wave index within the workgroup as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Per-lane constants of the score rule.
 struct TileConsts {
     float mul;        // NONE: scale*log2e; soft-cap exact path: 2*scale*log2e/cap
@@ -651,7 +654,7 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
                                                 f32x16_t (&o)[D / 32], RowState<false>& st, char* lds) {
     using G = Tiles<__bf16, D>;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = wave_id();
     const int sub_per_block = a.kv_block / kTileN;
     const bool with_doc = a.mask.kind == MASK_DOC_CAUSAL;
 
@@ -685,9 +688,11 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
         for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.v, (lds_void_t*)(buf + G::kElemsK * 2 + (i * 4 + wave) * 1024),
                                                      16, pl.v[i], vo, 0, 0);
-        if (with_doc && wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.doc, (lds_void_t*)(buf + G::kDocOffset), 4, lane * 4, kv0 * 4,
-                                                     0, 0);
+        if (with_doc && wave == 0) {
+            // lane id from mbcnt: cheap to recompute, so it is not kept live
+            const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.doc, (lds_void_t*)(buf + G::kDocOffset), 4, l4, kv0 * 4, 0, 0);
+        }
     };
     // DMA writes to LDS count on vmcnt: drain them before the barrier that
     // publishes the buffer.
@@ -870,11 +875,12 @@ __device__ __forceinline__ int lane_doc(const MaskArgs& m, int q_pos) {
     return (q_pos >= 0 && q_pos < m.doc_len) ? __ldg(m.doc_id + q_pos) : -2;
 }
 
-// Waves per SIMD the prefill kernel is compiled for: three at head dim 64 (the
-// score pipeline is VALU-bound there, so more waves hide MFMA and LDS latency
-// behind each other's VALU work), two at 128.
-template <typename T, int D> struct PrefillOccupancy {
-    static constexpr int value = sizeof(T) == 2 ? (D == 64 ? 3 : 2) : (D == 64 ? 2 : 1);
+// Waves per SIMD the prefill kernel is compiled for: four for bf16 key-split
+// workgroups at head dim 64 (the score pipeline is VALU-bound there, so more
+// waves hide MFMA and LDS latency behind each other's VALU work), otherwise
+// as many as the registers of the wider tiles allow.
+template <typename T, int D, bool KSPLIT> struct PrefillOccupancy {
+    static constexpr int value = sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? 4 : 3) : 2) : (D == 64 ? 2 : 1);
 };
 
 }  // namespace
@@ -899,7 +905,7 @@ namespace {
 // workgroup (short critical path when a few Q blocks hold most of the work);
 // otherwise a part is 128 rows, one 32-row group per wave, both key halves.
 template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT>
-__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D>::value)) void attn_fwd_prefill(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT>::value)) void attn_fwd_prefill(FwdArgs a) {
     using G = Tiles<T, D>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::kBufBytes];
     constexpr int kRows = KSPLIT ? 64 : 128;
@@ -918,7 +924,7 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D>::value)) void att
         bh = (xcd + 8 * (k / a.group)) * a.group + k % a.group;
     }
     const int b = bh / a.Hq, hq = bh % a.Hq, hkv = hq / a.group;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+    const int lane = threadIdx.x & 63, wave = wave_id(), hf = lane >> 5;
     const int rg = KSPLIT ? (wave & 1) : wave, kh = KSPLIT ? (wave >> 1) : 0;
     const int r_in_blk = part * kRows + rg * 32 + (lane & 31);
 
@@ -997,7 +1003,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_decode(FwdArgs a) {
     const int qb = unit % a.nQB;
     const int bk = unit / a.nQB;
     const int b = bk / a.Hkv, hkv = bk % a.Hkv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+    const int lane = threadIdx.x & 63, wave = wave_id(), hf = lane >> 5;
     const int rg = wave & 1, kh = wave >> 1;
     const int r = rg * 32 + (lane & 31);
     const int rows = a.group * a.q_block;
