@@ -114,6 +114,14 @@ __device__ __forceinline__ float wave_half_sum(float x) {
 
 template <typename T> struct Precise { static constexpr bool value = sizeof(T) == 4; };
 
+// Load of a wave-uniform address through the constant address space, which
+// the compiler serves with a scalar load (lgkmcnt), so it never waits behind
+// the vector-memory counter that tracks the tile DMA.
+__device__ __forceinline__ int scalar_load(const int* p) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) int*>(
+        reinterpret_cast<uintptr_t>(p));
+}
+
 // Wave index within the workgroup as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -642,10 +650,28 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
     }
 }
 
-// bf16 tile walk: tiles arrive by LDS-DMA (no staging registers), double
-// buffered, with the loop unrolled over the two buffers so every LDS operand
-// address is a per-lane constant plus an immediate.
-template <int D, int SCORE, bool FIXED, bool KSPLIT>
+// Calls f(integral_constant<int, I>) for I = FIRST .. LAST - 1.
+template <int FIRST, int LAST> struct Unroll {
+    template <class F> __device__ __forceinline__ static void run(F&& f) {
+        f(std::integral_constant<int, FIRST>{});
+        Unroll<FIRST + 1, LAST>::run(f);
+    }
+};
+template <int LAST> struct Unroll<LAST, LAST> {
+    template <class F> __device__ __forceinline__ static void run(F&&) {}
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// bf16 tile walk: tiles arrive by LDS-DMA (no staging registers) into a ring of
+// STAGES buffers, STAGES - 1 tiles ahead of the one being computed; the loop is
+// unrolled over the ring so every LDS operand address is a per-lane constant
+// plus an immediate.  Per tile: wait for this wave's part of the tile, barrier
+// (publishes the tile and frees the buffer computed last), refill that buffer
+// with the tile STAGES - 1 ahead, compute.
+template <int D, int SCORE, bool FIXED, bool KSPLIT, int STAGES>
 __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* __restrict__ kbase,
                                                 const __bf16* __restrict__ vbase, const QRegs<__bf16, D>& qr,
                                                 const int* __restrict__ part_idx, int n_part,
@@ -653,6 +679,7 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
                                                 const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
                                                 f32x16_t (&o)[D / 32], RowState<false>& st, char* lds) {
     using G = Tiles<__bf16, D>;
+    static_assert(STAGES >= 2, "at least double buffering");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = wave_id();
     const int sub_per_block = a.kv_block / kTileN;
@@ -662,8 +689,8 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
         const int blk = sub_per_block == 1 ? t : t / sub_per_block;
         const int sub = t - blk * sub_per_block;
         int kb;
-        if (blk < n_part) { kb = part_idx[blk]; masked = true; }
-        else { kb = full_idx[blk - n_part]; masked = false; }
+        if (blk < n_part) { kb = scalar_load(part_idx + blk); masked = true; }
+        else { kb = scalar_load(full_idx + (blk - n_part)); masked = false; }
         return kb * a.kv_block + sub * kTileN;
     };
 
@@ -678,6 +705,8 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     // key-split waves read only their own key half: fold it into the offsets
     const LdsAddr<__bf16, D> la = lds_addr_bf16<D>(lane, KSPLIT ? kh : 0);
 
+    // K and V instructions per wave and tile (wave 0 adds one doc-id load).
+    constexpr int kPerTile = 2 * DmaPlan<D>::kInsts;
     auto issue = [&](char* buf, int kv0) {
         const int ko = kv0 * sr.k_row_bytes, vo = kv0 * sr.v_row_bytes;
 #pragma unroll
@@ -694,27 +723,37 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.doc, (lds_void_t*)(buf + G::kDocOffset), 4, l4, kv0 * 4, 0, 0);
         }
     };
-    // DMA writes to LDS count on vmcnt: drain them before the barrier that
-    // publishes the buffer.
-    auto publish = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
 
-    bool masked;
-    int kv0 = tile_kv0(tile_lo, masked);
-    issue(lds, kv0);
-    publish();
+    // Tile descriptors of the ring (static indices after unrolling).
+    int ring_kv0[STAGES];
+    bool ring_masked[STAGES];
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i) {
+        ring_masked[i] = false;
+        ring_kv0[i] = 0;
+        if (tile_lo + i < tile_hi) {
+            ring_kv0[i] = tile_kv0(tile_lo + i, ring_masked[i]);
+            issue(lds + i * G::kBufBytes, ring_kv0[i]);
+        }
+    }
     auto step = [&](auto bufc, int t) {
         constexpr int B = decltype(bufc)::value;
-        bool next_masked = false;
-        int next_kv0 = 0;
-        const bool has_next = t + 1 < tile_hi;
-        if (has_next) {
-            next_kv0 = tile_kv0(t + 1, next_masked);
-            issue(lds + (B ^ 1) * G::kBufBytes, next_kv0);
+        constexpr int R = (B + STAGES - 1) % STAGES;     // buffer computed last, refilled now
+        // Tiles t+1 .. t+STAGES-2 may stay in flight (DMA completes in order;
+        // wave 0's doc loads make it wait a little longer than needed).
+        if (t + STAGES - 2 < tile_hi) __builtin_amdgcn_s_waitcnt(vmcnt_imm((STAGES - 2) * kPerTile));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // A bare barrier: the waves' LDS reads of the buffer refilled below were
+        // consumed (waited on) before they got here, and a fenced barrier would
+        // also drain the DMA still in flight for later tiles.
+        __builtin_amdgcn_s_barrier();
+        if (t + STAGES - 1 < tile_hi) {
+            ring_kv0[R] = tile_kv0(t + STAGES - 1, ring_masked[R]);
+            issue(lds + R * G::kBufBytes, ring_kv0[R]);
         }
         const char* cur = lds + B * G::kBufBytes;
+        const int kv0 = ring_kv0[B];
+        const bool masked = ring_masked[B];
         if (wave_active) {
             if constexpr (KSPLIT) {
                 process_tile<__bf16, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, kh, 0,
@@ -724,28 +763,29 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
                 process_tile<__bf16, D, SCORE, FIXED>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 1, 1, lane);
             }
         }
-        publish();
-        kv0 = next_kv0;
-        masked = next_masked;
     };
-    for (int t = tile_lo; t < tile_hi; t += 2) {
-        step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < tile_hi) step(std::integral_constant<int, 1>{}, t + 1);
+    for (int t = tile_lo; t < tile_hi; t += STAGES) {
+        Unroll<0, STAGES>::run([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            if (t + I < tile_hi) step(ic, t + I);
+        });
     }
+    // every wave is done with the ring before the caller reuses the LDS
+    __syncthreads();
 }
 
 // Walk tiles [tile_lo, tile_hi) of one row block's lists: partial tiles (masked)
 // first, then full tiles.  All waves load; active waves compute either key half
 // kh of every tile (KSPLIT) or both halves.
-template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT>
+template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, int STAGES = 2>
 __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restrict__ kbase, const T* __restrict__ vbase,
                                             const QRegs<T, D>& qr, const int* __restrict__ part_idx, int n_part,
                                             const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                             const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
                                             f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds) {
     if constexpr (sizeof(T) == 2) {
-        attend_rows_dma<D, SCORE, FIXED, KSPLIT>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo, tile_hi, tc,
-                                                 row, wave_active, kh, o, st, lds);
+        attend_rows_dma<D, SCORE, FIXED, KSPLIT, STAGES>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
+                                                         tile_hi, tc, row, wave_active, kh, o, st, lds);
     } else {
     using G = Tiles<T, D>;
     const LdsAddr<T, D> la{};
@@ -758,8 +798,8 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
         const int blk = sub_per_block == 1 ? t : t / sub_per_block;
         const int sub = t - blk * sub_per_block;
         int kb;
-        if (blk < n_part) { kb = part_idx[blk]; masked = true; }
-        else { kb = full_idx[blk - n_part]; masked = false; }
+        if (blk < n_part) { kb = scalar_load(part_idx + blk); masked = true; }
+        else { kb = scalar_load(full_idx + (blk - n_part)); masked = false; }
         return kb * a.kv_block + sub * kTileN;
     };
 
@@ -945,8 +985,8 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT>::value)) 
 
     const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
     const int64_t row_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nQB + qb;
-    const int n_part = min(max(a.kv_num[row_id], 0), a.nKB);
-    const int n_full = min(max(a.full_num[row_id], 0), a.nKB - n_part);
+    const int n_part = min(max(scalar_load(a.kv_num + row_id), 0), a.nKB);
+    const int n_full = min(max(scalar_load(a.full_num + row_id), 0), a.nKB - n_part);
     const int n_tiles = (n_part + n_full) * (a.kv_block / kTileN);
 
     const TileConsts tc = make_consts(a, hq);
@@ -986,6 +1026,16 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT>::value)) 
     }
 }
 
+// Decode streams K/V once, so it is bound by HBM latency x bytes in flight:
+// a ring of four tile buffers keeps three tiles (96 KiB at head dim 128) in
+// flight per workgroup, which fills the LDS of a CU at one workgroup (two at
+// head dim 64).
+template <int D> struct DecodeShape {
+    static constexpr int kStages = 4;
+    static constexpr int kWgsPerCu = D == 64 ? 2 : 1;
+    static constexpr int kWavesPerSimd = kWgsPerCu;   // 4 waves per workgroup, one per SIMD
+};
+
 // Decode / verify: one workgroup per (split, Q block, K/V head, batch).  Rows
 // are the G query heads sharing the K/V head times the Q block's queries
 // (row r -> head hkv*G + r / q_block, query qb*q_block + r % q_block), so every
@@ -994,10 +1044,10 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT>::value)) 
 // numerator, base-2 reference and denominator.  bf16 only; the block mask must
 // be the same for every head (H = 1).
 template <int D, int SCORE, bool FIXED>
-__global__ __launch_bounds__(kThreads) void attn_fwd_decode(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_fwd_decode(FwdArgs a) {
     using T = __bf16;
     using G = Tiles<T, D>;
-    __shared__ __attribute__((aligned(16))) char lds[2 * G::kBufBytes];
+    __shared__ __attribute__((aligned(16))) char lds[DecodeShape<D>::kStages * G::kBufBytes];
     const int split = blockIdx.x % a.splits;
     const int unit = blockIdx.x / a.splits;
     const int qb = unit % a.nQB;
@@ -1026,8 +1076,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_decode(FwdArgs a) {
 
     const int bm_b = a.Bm > 1 ? b : 0;
     const int64_t row_id = (int64_t)bm_b * a.nQB + qb;
-    const int n_part = min(max(a.kv_num[row_id], 0), a.nKB);
-    const int n_full = min(max(a.full_num[row_id], 0), a.nKB - n_part);
+    const int n_part = min(max(scalar_load(a.kv_num + row_id), 0), a.nKB);
+    const int n_full = min(max(scalar_load(a.full_num + row_id), 0), a.nKB - n_part);
     const int n_tiles = (n_part + n_full) * (a.kv_block / kTileN);
     const int t_lo = (int)((int64_t)n_tiles * split / a.splits);
     const int t_hi = (int)((int64_t)n_tiles * (split + 1) / a.splits);
@@ -1037,8 +1087,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_decode(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     RowState<false> st{kNegInf, 0.0f, 0.0f};
-    attend_rows<T, D, SCORE, FIXED, true>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB, n_part,
-                                          a.full_idx + row_id * a.nKB, t_lo, t_hi, tc, row, wave_active, kh, o, st, lds);
+    attend_rows<T, D, SCORE, FIXED, true, DecodeShape<D>::kStages>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
+                                                                   n_part, a.full_idx + row_id * a.nKB, t_lo, t_hi,
+                                                                   tc, row, wave_active, kh, o, st, lds);
     merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
 
     const float l = wave_half_sum(st.l);
@@ -1152,8 +1203,6 @@ hipError_t dispatch(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, int kv_block, int nKB, int Hm) {
-    (void)L;
-    (void)D;
     if (dtype != 1 || Hm != 1 || Hq % Hkv != 0) return 0;
     const int group = Hq / Hkv;
     if ((int64_t)group * q_block > 64 || q_block > 32) return 0;
@@ -1161,7 +1210,9 @@ int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, 
     const int64_t units = (int64_t)B * Hkv * n_qb;
     const int64_t tiles = (int64_t)nKB * (kv_block / kTileN);
     if (units >= 1024 || tiles < 32) return 0;
-    int64_t splits = 2048 / units;
+    // one workgroup per resident slot of the chip (256 CUs)
+    const int64_t slots = 256 * (D == 64 ? DecodeShape<64>::kWgsPerCu : DecodeShape<128>::kWgsPerCu);
+    int64_t splits = slots / units;
     splits = std::min<int64_t>(splits, tiles / 16);
     splits = std::max<int64_t>(std::min<int64_t>(splits, 256), 1);
     return (int)splits;

@@ -231,6 +231,32 @@ def test_softcap_tiers_by_score_magnitude(dev, mask_kind, score):
     assert_attention_close(out, lse, out_ref, lse_ref, "bf16", f"tiers {score} {mask_kind}")
 
 
+# Short query blocks against long key ranges take the GQA-packed split-KV
+# decode kernel (query heads of one K/V head packed into the rows, key range
+# split across workgroups, partials merged by the combine kernel).  Rows with
+# only a few visible tiles give split ranges of zero, one or two tiles.
+DECODE_CASES = [
+    # G, q_block, L, S, mask, score
+    (4, 16, 16, 4100, dict(mask_kind="causal"), dict(kind="softcap", cap=50.0)),
+    (2, 16, 21, 3000, dict(mask_kind="causal_window_sinks", window=70, sinks=3),
+     dict(kind="softcap_alibi", cap=30.0, alibi_m=8.0)),
+    (2, 32, 40, 2600, dict(mask_kind="doc_causal"), dict(kind="none")),
+    (1, 32, 7, 2100, dict(mask_kind="noop"), dict(kind="softcap", cap=5.0)),
+    (4, 16, 33, 2500, dict(mask_kind="causal_window_sinks", window=300, sinks=0), dict(kind="none")),
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_split_kv_paths(dev, D):
+    for i, (G, qb, L, S, mask, score) in enumerate(DECODE_CASES):
+        B, Hkv = 2, 2
+        probe = pbs.flex_blockmask_build(pbs.MaskSpec(kind="causal", q_offset=S - L), L, S, qb, 64, device=dev)
+        assert pbs.flex_attn_fwd_workspace_bytes(torch.bfloat16, B, G * Hkv, Hkv, L, S, D, probe) > 0, \
+            "case does not take the split-KV decode path"
+        run_case(dev, seed=300 + i + D, dtype="bf16", B=B, Hq=G * Hkv, Hkv=Hkv, L=L, S=S, D=D, qb=qb, kb=64,
+                 score=score, what=f"decode D={D} G={G} qb={qb} L={L} S={S} {mask} {score}", **mask)
+
+
 def test_lse_optional_and_strided_inputs(dev):
     rng = np.random.default_rng(11)
     B, H, L, S, D = 2, 4, 190, 190, 64
