@@ -69,6 +69,26 @@ constexpr double kLin1 = -0.32320621727400445;
 constexpr double kLinErr = 7.9e-6;
 constexpr double kPolyScoreErr = 2.5e-4;
 
+}  // namespace
+
+ScoreConsts score_consts(float scale_f, float cap_f, int score_kind) {
+    ScoreConsts c{};
+    const double scale = scale_f, cap = cap_f, l2e = 1.4426950408889634;
+    c.mul = score_kind == SCORE_NONE ? (float)(scale * l2e) : (float)(2.0 * scale * l2e / cap);
+    c.c2 = (float)(cap * l2e);
+    const double r = scale / cap;
+    c.k0 = (float)(scale * l2e * kTanh0);
+    c.k1 = (float)(scale * l2e * kTanh1 * r * r);
+    c.k2 = (float)(scale * l2e * kTanh2 * r * r * r * r);
+    c.amax = (float)(kTanhRange / r);
+    c.j0 = (float)(scale * l2e * kLin0);
+    c.j1 = (float)(scale * l2e * kLin1 * r * r);
+    c.amax1 = cap * kLinErr <= kPolyScoreErr ? (float)(kLinRange / r) : 0.0f;
+    return c;
+}
+
+namespace {
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     static constexpr int kChunk = 4;     // elements per 16-byte load
@@ -138,28 +158,34 @@ struct TileConsts {
     double scale_d, cap_d, alpha_d;
 };
 
+template <bool PRECISE>
 __device__ __forceinline__ TileConsts make_consts(const FwdArgs& a, int hq) {
     TileConsts c;
-    const double scale = a.scale, cap = a.cap, l2e = 1.4426950408889634;
-    c.scale_d = scale;
-    c.cap_d = cap;
-    c.mul = a.score_kind == SCORE_NONE ? (float)(scale * l2e) : (float)(2.0 * scale * l2e / cap);
-    c.c2 = (float)(cap * l2e);
-    const double r = scale / cap;
-    c.k0 = (float)(scale * l2e * kTanh0);
-    c.k1 = (float)(scale * l2e * kTanh1 * r * r);
-    c.k2 = (float)(scale * l2e * kTanh2 * r * r * r * r);
-    c.amax = (float)(kTanhRange / r);
-    c.j0 = (float)(scale * l2e * kLin0);
-    c.j1 = (float)(scale * l2e * kLin1 * r * r);
-    c.amax1 = cap * kLinErr <= kPolyScoreErr ? (float)(kLinRange / r) : 0.0f;
+    c.mul = a.sc.mul;
+    c.c2 = a.sc.c2;
+    c.k0 = a.sc.k0;
+    c.k1 = a.sc.k1;
+    c.k2 = a.sc.k2;
+    c.amax = a.sc.amax;
+    c.j0 = a.sc.j0;
+    c.j1 = a.sc.j1;
+    c.amax1 = a.sc.amax1;
+    c.ref_fixed = a.ref_fixed;
+    c.scale_d = a.scale;
+    c.cap_d = a.cap;
     c.alpha_d = 0.0;
     c.alpha2 = 0.0f;
     if (a.score_kind == SCORE_SOFTCAP_ALIBI) {
-        c.alpha_d = exp2(-(double)a.alibi_m * (double)(hq + 1) / (double)a.Hq);
-        c.alpha2 = (float)(c.alpha_d * l2e);
+        // slope 2^(-m (h+1) / Hq) of this query head; the bf16 path needs it in
+        // fp32 only (its relative error scales the bias, so it is smallest
+        // where the weights are largest), the precise path in double
+        if constexpr (PRECISE) {
+            c.alpha_d = exp2(-(double)a.alibi_m * (double)(hq + 1) / (double)a.Hq);
+        } else {
+            const float e = -(a.alibi_m * (float)(hq + 1)) / (float)a.Hq;
+            c.alpha2 = __builtin_amdgcn_exp2f(e) * kLog2e;
+        }
     }
-    c.ref_fixed = a.ref_fixed;
     return c;
 }
 
@@ -989,7 +1015,7 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT>::value)) 
     const int n_full = min(max(scalar_load(a.full_num + row_id), 0), a.nKB - n_part);
     const int n_tiles = (n_part + n_full) * (a.kv_block / kTileN);
 
-    const TileConsts tc = make_consts(a, hq);
+    const TileConsts tc = make_consts<Precise<T>::value>(a, hq);
     f32x16_t o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
@@ -1082,7 +1108,7 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
     const int t_lo = (int)((int64_t)n_tiles * split / a.splits);
     const int t_hi = (int)((int64_t)n_tiles * (split + 1) / a.splits);
 
-    const TileConsts tc = make_consts(a, row.hq);
+    const TileConsts tc = make_consts<false>(a, row.hq);
     f32x16_t o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};

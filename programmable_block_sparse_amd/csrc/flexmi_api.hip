@@ -236,6 +236,7 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
     a.score_kind = score->kind;
     a.cap = score->kind == FLEX_SCORE_NONE ? 1.0f : score->cap;
     a.alibi_m = score->alibi_m;
+    a.sc = score_consts(a.scale, a.cap, a.score_kind);
     a.mask = to_mask_args(mask);
     a.kv_num = bm->kv_num_blocks;
     a.kv_idx = bm->kv_indices;

@@ -23,6 +23,17 @@ struct BuildArgs {
 
 hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream);
 
+// Constants of the score rule that depend only on scale and cap (computed on
+// the host in double, rounded once).  Base-2 units: log2(e) is folded in.
+struct ScoreConsts {
+    float mul;        // NONE: scale*log2e; soft-cap exact path: 2*scale*log2e/cap
+    float c2;         // cap*log2e
+    float k0, k1, k2; // quintic path: g2 = acc*(k0 + k1*w + k2*w^2), w = acc^2
+    float amax;       // quintic valid while |acc| <= amax
+    float j0, j1;     // cubic path: g2 = acc*(j0 + j1*w)
+    float amax1;      // cubic valid while |acc| <= amax1 (0 when the cap is too large)
+};
+
 // Forward pass arguments (element strides; last dim contiguous).
 struct FwdArgs {
     const void* q;
@@ -39,6 +50,7 @@ struct FwdArgs {
     int score_kind;
     float cap;
     float alibi_m;
+    ScoreConsts sc;
     // mask_mod
     MaskArgs mask;
     // block mask
@@ -64,6 +76,9 @@ int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D);
 
 // Number of key-range splits of the GQA-packed decode kernel for these sizes,
 // or 0 when the prefill kernel is used.
+// Host-side constants of the score rule for this scale and cap.
+ScoreConsts score_consts(float scale, float cap, int score_kind);
+
 int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, int kv_block, int nKB, int Hm);
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for an unsupported
