@@ -68,13 +68,57 @@ typedef enum { FLEX_F32 = 0, FLEX_BF16 = 1 } flex_dtype;
  *                        first `sinks` keys (tensorcad "Attention expressions",
  *                        Examples, sink window)
  *   DOC_CAUSAL           j <= p and doc_id[p] == doc_id[j] (charlestar blog,
- *                        packing section; quant67 article section 7 demo) */
+ *                        packing section; quant67 article section 7 demo)
+ *   PROGRAM              an AND of up to FLEX_MAX_CLAUSES clauses, each an OR
+ *                        of up to FLEX_MAX_LITERALS predicates from the
+ *                        flex_pred_kind list below: the and_masks / or_masks
+ *                        composition of the 2kiu guide, section 4.3 (an AND
+ *                        folds from true, an OR from false), which expresses
+ *                        the mask column of the tensorcad "Attention
+ *                        expressions" Examples table (prefix-LM, sink window,
+ *                        chunked, every k-th key, half the heads global) */
 typedef enum {
     FLEX_MASK_NOOP = 0,
     FLEX_MASK_CAUSAL = 1,
     FLEX_MASK_CAUSAL_WINDOW_SINKS = 2,
-    FLEX_MASK_DOC_CAUSAL = 3
+    FLEX_MASK_DOC_CAUSAL = 3,
+    FLEX_MASK_PROGRAM = 4
 } flex_mask_kind;
+
+/* Predicates of a PROGRAM mask, on query position p (= row + q_offset), key j
+ * and query head h:
+ *   CAUSAL   j <= p
+ *   WINDOW   p - j < arg                      (arg >= 1)
+ *   KV_LT    j < arg                          (arg >= 0)
+ *   CHUNK    floor(p / arg) == floor(j / arg) (arg >= 1, floor division)
+ *   STRIDE   (p - j) mod arg == 0             (arg >= 1)
+ *   DOC      doc_id[p] == doc_id[j]; positions outside doc_id are in no
+ *            document (doc_id and doc_len as for DOC_CAUSAL, q_offset >= 0)
+ *   HEAD_LT  h < arg                          (arg >= 0); a mask that uses it
+ *            reads the head, so its BlockMask must have H = Hq */
+typedef enum {
+    FLEX_PRED_CAUSAL = 0,
+    FLEX_PRED_WINDOW = 1,
+    FLEX_PRED_KV_LT = 2,
+    FLEX_PRED_CHUNK = 3,
+    FLEX_PRED_STRIDE = 4,
+    FLEX_PRED_DOC = 5,
+    FLEX_PRED_HEAD_LT = 6
+} flex_pred_kind;
+
+#define FLEX_MAX_CLAUSES 4
+#define FLEX_MAX_LITERALS 2
+
+typedef struct {
+    int32_t kind;   /* a flex_pred_kind */
+    int32_t arg;
+} flex_mask_pred;
+
+/* A clause holds when any of its n (1..FLEX_MAX_LITERALS) predicates does. */
+typedef struct {
+    int32_t n;
+    flex_mask_pred lit[FLEX_MAX_LITERALS];
+} flex_mask_clause;
 
 /* score_mod menu, applied to the already scaled score s of every computed cell
  * (full and partial tiles alike) before the mask.
@@ -83,11 +127,14 @@ typedef enum {
  *   SOFTCAP_ALIBI   g = cap * tanh(s / cap) + alpha_h * (j - p),
  *                   alpha_h = 2^(-alibi_m * (h + 1) / Hq), h the query head
  *                   (charlestar blog, score_mod ordering section: cap first,
- *                   bias after; tensorcad Examples, ALiBi slope) */
+ *                   bias after; tensorcad Examples, ALiBi slope)
+ *   ALIBI           g = s + alpha_h * (j - p), alpha_h as above, no cap
+ *                   (tensorcad Examples, the ALiBi row) */
 typedef enum {
     FLEX_SCORE_NONE = 0,
     FLEX_SCORE_SOFTCAP = 1,
-    FLEX_SCORE_SOFTCAP_ALIBI = 2
+    FLEX_SCORE_SOFTCAP_ALIBI = 2,
+    FLEX_SCORE_ALIBI = 3
 } flex_score_kind;
 
 /* Mask parameters (host struct).
@@ -96,9 +143,12 @@ typedef enum {
  *   sinks     CAUSAL_WINDOW_SINKS: number of always-visible leading keys, >= 0
  *   q_offset  logical position of query row 0 (S - L aligns the causal
  *             diagonal bottom-right; 0 aligns it top-left)
- *   doc_id    DOC_CAUSAL: device int32[doc_len], document index per position
- *   doc_len   DOC_CAUSAL: must cover every key and query position, i.e.
- *             doc_len >= max(S, q_offset + L) with q_offset >= 0 */
+ *   doc_id    DOC_CAUSAL and the DOC predicate: device int32[doc_len],
+ *             document index per position
+ *   doc_len   must then cover every key and query position, i.e.
+ *             doc_len >= max(S, q_offset + L) with q_offset >= 0
+ *   n_clauses, clause   PROGRAM: 1 <= n_clauses <= FLEX_MAX_CLAUSES clauses,
+ *             all of which must hold */
 typedef struct {
     int32_t kind;
     int32_t window;
@@ -107,9 +157,12 @@ typedef struct {
     int64_t q_offset;
     const int32_t* doc_id;
     int64_t doc_len;
+    int32_t n_clauses;
+    flex_mask_clause clause[FLEX_MAX_CLAUSES];
 } flex_mask_params;
 
-/* Score parameters (host struct).  cap > 0 for the SOFTCAP kinds. */
+/* Score parameters (host struct).  cap > 0 for the SOFTCAP kinds; alibi_m
+ * (the slope exponent, 8 in the pages' examples) for the ALiBi kinds. */
 typedef struct {
     int32_t kind;
     float cap;
@@ -189,6 +242,20 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
                           const flex_score_params* score, const flex_mask_params* mask,
                           const flex_block_mask* bm, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* flex_attn_fwd with the auxiliary outputs of the 2kiu guide, section 2:
+ *   max_scores   device float32 (B,Hq,L) contiguous, or NULL: the largest
+ *                visible score g(s) of each row (natural units, after
+ *                score_mod and the mask), -inf for rows with no visible key
+ * Every other argument is as for flex_attn_fwd, which is this call with
+ * max_scores = NULL. */
+flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32_t dtype,
+                              int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D,
+                              const int64_t q_strides[3], const int64_t k_strides[3],
+                              const int64_t v_strides[3], float scale,
+                              const flex_score_params* score, const flex_mask_params* mask,
+                              const flex_block_mask* bm, void* out, float* lse, float* max_scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* flex_status_string(int32_t status);

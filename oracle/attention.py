@@ -7,7 +7,9 @@ the softmax-weighted sum of v_j over visible j.  The blog states this for rows
 with at least one visible key; for a row with none (the quant67 causal-mask
 article, section 7 on -inf numerics, shows the naive formula gives NaN) the
 reading used here is out = 0 and lse = -inf.  lse is the natural log of the
-softmax denominator (2kiu guide, section 2: auxiliary lse of shape (B, Hq, L)).
+softmax denominator (2kiu guide, section 2: auxiliary lse of shape (B, Hq, L));
+the same section's other auxiliary output, max_scores, is read as the largest
+score entering the softmax of each row (-inf for rows with no visible key).
 
 Grouped-query attention (2kiu guide, section 6.1): query head hq reads K/V
 head hq // (Hq / Hkv).  Query row i has logical position i + q_offset (blog,
@@ -42,8 +44,9 @@ def _rows_softmax(z: np.ndarray, vis: np.ndarray, V: np.ndarray):
 
 
 def attention_rows(q_rows, K, V, *, b: int, hq: int, Hq: int, row_ids, scale: float,
-                   score: ScoreMod, mask: MaskMod, q_offset: int):
-    """out (n, D) and lse (n,) for the given query rows of one (batch, query head).
+                   score: ScoreMod, mask: MaskMod, q_offset: int, with_max: bool = False):
+    """out (n, D) and lse (n,) for the given query rows of one (batch, query head),
+    plus the row maxima of the masked scores when ``with_max``.
 
     q_rows: (n, D) query vectors of rows ``row_ids``; K, V: (S, D) of the matching
     K/V head.  ``scale`` is applied to q.k before g.
@@ -58,15 +61,19 @@ def attention_rows(q_rows, K, V, *, b: int, hq: int, Hq: int, row_ids, scale: fl
     g = score(s, b, hq, q_pos, kv, Hq)
     vis = mask(b, hq, q_pos, kv)
     z = np.where(vis, g, -np.inf)
-    return _rows_softmax(z, vis, V)
+    out, lse = _rows_softmax(z, vis, V)
+    if with_max:
+        return out, lse, z.max(axis=1)
+    return out, lse
 
 
 def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int,
-              rows=None, heads=None, batches=None, row_chunk: int = 512):
+              rows=None, heads=None, batches=None, row_chunk: int = 512, with_max: bool = False):
     """Dense oracle over (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values.
 
     Returns ``out`` (nb, nh, nr, D) and ``lse`` (nb, nh, nr) in float64 for the selected
-    batches / query heads / query rows (all of them by default).
+    batches / query heads / query rows (all of them by default), and the row
+    maxima ``max_scores`` (nb, nh, nr) as a third value when ``with_max``.
     """
     B, Hq, L, D = q.shape
     Hkv = k.shape[1]
@@ -79,6 +86,7 @@ def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset
     Dv = v.shape[-1]
     out = np.zeros((len(batches), len(heads), len(rows), Dv), dtype=np.float64)
     lse = np.zeros((len(batches), len(heads), len(rows)), dtype=np.float64)
+    mx = np.zeros((len(batches), len(heads), len(rows)), dtype=np.float64)
     for bi, b in enumerate(batches):
         for hi, hq in enumerate(heads):
             hkv = hq // group
@@ -86,8 +94,11 @@ def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset
             V = np.asarray(v[b, hkv], dtype=np.float64)
             for c0 in range(0, len(rows), row_chunk):
                 rid = rows[c0:c0 + row_chunk]
-                o, ls = attention_rows(q[b, hq][rid], K, V, b=b, hq=hq, Hq=Hq, row_ids=rid,
-                                       scale=scale, score=score, mask=mask, q_offset=q_offset)
+                o, ls, m = attention_rows(q[b, hq][rid], K, V, b=b, hq=hq, Hq=Hq, row_ids=rid,
+                                          scale=scale, score=score, mask=mask, q_offset=q_offset, with_max=True)
                 out[bi, hi, c0:c0 + len(rid)] = o
                 lse[bi, hi, c0:c0 + len(rid)] = ls
+                mx[bi, hi, c0:c0 + len(rid)] = m
+    if with_max:
+        return out, lse, mx
     return out, lse

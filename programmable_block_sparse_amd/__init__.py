@@ -7,6 +7,7 @@ the same names:
 
   flex_blockmask_build(mask, L, S, q_block, kv_block, ...) -> BlockMask
   flex_attn_fwd(q, k, v, score=..., mask=..., block_mask=..., ...) -> (out, lse)
+  flex_attn_fwd_aux(q, k, v, ...) -> (out, lse, max_scores)
   flex_attn_fwd_workspace_bytes(...)
   flex_status_string(code)
 
@@ -25,22 +26,33 @@ import torch  # imported first so the library binds to torch's HIP runtime
 
 __all__ = [
     "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
-    "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_workspace_bytes", "flex_status_string",
-    "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "EXPORTED_SYMBOLS",
+    "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_aux", "flex_attn_fwd_workspace_bytes",
+    "flex_status_string", "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "PREDICATES", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-MASK_KINDS = {"noop": 0, "causal": 1, "causal_window_sinks": 2, "doc_causal": 3}
-SCORE_KINDS = {"none": 0, "softcap": 1, "softcap_alibi": 2}
+MASK_KINDS = {"noop": 0, "causal": 1, "causal_window_sinks": 2, "doc_causal": 3, "program": 4}
+SCORE_KINDS = {"none": 0, "softcap": 1, "softcap_alibi": 2, "alibi": 3}
+PREDICATES = {"causal": 0, "window": 1, "kv_lt": 2, "chunk": 3, "stride": 4, "doc": 5, "head_lt": 6}
+MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd",
+EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
                     "flex_status_string", "flex_last_error")
+
+
+class flex_mask_pred(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("arg", ctypes.c_int32)]
+
+
+class flex_mask_clause(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("lit", flex_mask_pred * MAX_LITERALS)]
 
 
 class flex_mask_params(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32), ("sinks", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("doc_id", ctypes.c_void_p),
-                ("doc_len", ctypes.c_int64)]
+                ("doc_len", ctypes.c_int64), ("n_clauses", ctypes.c_int32),
+                ("clause", flex_mask_clause * MAX_CLAUSES)]
 
 
 class flex_score_params(ctypes.Structure):
@@ -81,6 +93,11 @@ def load_library():
                                   ctypes.POINTER(flex_score_params), ctypes.POINTER(flex_mask_params),
                                   ctypes.POINTER(flex_block_mask), P, P, P, ctypes.c_size_t, P]
     lib.flex_attn_fwd.restype = ctypes.c_int
+    lib.flex_attn_fwd_aux.argtypes = [P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3,
+                                      ctypes.c_float, ctypes.POINTER(flex_score_params),
+                                      ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask), P, P, P,
+                                      P, ctypes.c_size_t, P]
+    lib.flex_attn_fwd_aux.restype = ctypes.c_int
     lib.flex_status_string.argtypes = [I32]
     lib.flex_status_string.restype = ctypes.c_char_p
     lib.flex_last_error.argtypes = []
@@ -110,16 +127,22 @@ def _check(status: int):
 
 @dataclasses.dataclass
 class MaskSpec:
-    """mask_mod menu entry.  ``q_offset=None`` means bottom-right alignment (S - L)."""
+    """mask_mod menu entry.  ``q_offset=None`` means bottom-right alignment (S - L).
+
+    kind "program": ``clauses`` is a sequence of clauses, each a sequence of
+    (predicate, argument) pairs from PREDICATES; the mask is the AND of the
+    clauses, a clause the OR of its predicates (and_masks / or_masks)."""
     kind: str = "noop"
     window: int = 0
     sinks: int = 0
     q_offset: Optional[int] = None
-    doc_id: Optional[torch.Tensor] = None   # int32 device tensor for "doc_causal"
+    doc_id: Optional[torch.Tensor] = None   # int32 device tensor for "doc_causal" / the "doc" predicate
+    clauses: tuple = ()
 
     def to_c(self, L: int, S: int) -> flex_mask_params:
         key = (L, S, self.kind, self.window, self.sinks, self.q_offset,
-               None if self.doc_id is None else (self.doc_id.data_ptr(), self.doc_id.numel()))
+               None if self.doc_id is None else (self.doc_id.data_ptr(), self.doc_id.numel()),
+               tuple(tuple((str(n), int(a)) for n, a in c) for c in self.clauses))
         cached = self.__dict__.get("_c")
         if cached is not None and cached[0] == key:
             return cached[1]
@@ -133,6 +156,15 @@ class MaskSpec:
                 raise ValueError("doc_id must be a contiguous int32 tensor")
             m.doc_id = self.doc_id.data_ptr()
             m.doc_len = self.doc_id.numel()
+        clauses = key[-1]
+        if len(clauses) > MAX_CLAUSES or any(len(c) > MAX_LITERALS for c in clauses):
+            raise ValueError(f"at most {MAX_CLAUSES} clauses of at most {MAX_LITERALS} predicates")
+        m.n_clauses = len(clauses)
+        for i, c in enumerate(clauses):
+            m.clause[i].n = len(c)
+            for j, (name, arg) in enumerate(c):
+                m.clause[i].lit[j].kind = PREDICATES[name]
+                m.clause[i].lit[j].arg = arg
         self.__dict__["_c"] = (key, m)
         return m
 
@@ -237,6 +269,23 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_ma
     bfloat16) with a contiguous last dim.  Returns (out, lse); lse is None when
     ``return_lse`` is false.  ``scale=None`` selects 1/sqrt(D).
     """
+    out, lse, _ = _fwd(q, k, v, block_mask, score, mask, scale, return_lse, False, out, lse, None, workspace)
+    return out, lse
+
+
+def flex_attn_fwd_aux(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_mask: BlockMask,
+                      score: Optional[ScoreSpec] = None, mask: Optional[MaskSpec] = None,
+                      scale: Optional[float] = None, return_lse: bool = True, return_max_scores: bool = True,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      max_scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """flex_attn_fwd plus the per-row maximum visible score (C: flex_attn_fwd_aux).
+
+    Returns (out, lse, max_scores); an output not requested is None."""
+    return _fwd(q, k, v, block_mask, score, mask, scale, return_lse, return_max_scores, out, lse, max_scores,
+                workspace)
+
+
+def _fwd(q, k, v, block_mask, score, mask, scale, return_lse, return_max, out, lse, max_scores, workspace):
     lib = load_library()
     score = score or ScoreSpec()
     mask = mask or MaskSpec()
@@ -257,19 +306,26 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_ma
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
+    if return_max and max_scores is None:
+        max_scores = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if not return_max:
+        max_scores = None
     cbm = block_mask.to_c()
     ws_bytes = int(lib.flex_attn_fwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     cs, cm = score.to_c(), mask.to_c(L, S)
-    status = lib.flex_attn_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
-        ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs), ctypes.byref(cm),
-        ctypes.byref(cbm), out.data_ptr(), None if lse is None else lse.data_ptr(),
-        None if not ws_bytes else workspace.data_ptr(), ws_bytes, ctypes.c_void_p(_stream_ptr(q.device)))
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
+            ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs), ctypes.byref(cm),
+            ctypes.byref(cbm), out.data_ptr(), None if lse is None else lse.data_ptr()]
+    tail = [None if not ws_bytes else workspace.data_ptr(), ws_bytes, ctypes.c_void_p(_stream_ptr(q.device))]
+    if max_scores is None:
+        status = lib.flex_attn_fwd(*args, *tail)
+    else:
+        status = lib.flex_attn_fwd_aux(*args, max_scores.data_ptr(), *tail)
     _check(status)
-    return out, lse
+    return out, lse, max_scores
 
 
 def default_scale(D: int) -> float:

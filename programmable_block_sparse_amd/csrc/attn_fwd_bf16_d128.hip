@@ -1,0 +1,12 @@
+// Forward kernels instantiated for bf16 inputs at head dimension 128 (one
+// translation unit per dtype and head dimension so they compile in parallel).
+#include "attn_fwd_impl.hpp"
+
+namespace flexmi {
+
+hipError_t launch_attn_fwd_bf16_d128(const FwdArgs& a, hipStream_t stream) {
+    if (a.splits > 0) return dispatch<__bf16, 128, true>(a, stream);
+    return dispatch<__bf16, 128, false>(a, stream);
+}
+
+}  // namespace flexmi

@@ -37,9 +37,61 @@ enum : int { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2, TILE_COUNT = 3 };
 // to be counted.  Rows [r0, r1] (logical positions p0 = r0 + off, p1), columns
 // [c0, c1], all clipped to L and S; `clipped` tells whether the tile extends
 // past L or S (then it cannot be full).
+// Three-valued truth of a PROGRAM predicate over the rectangle of positions
+// [p0, p1] x keys [c0, c1] at head h: all cells true, all false, or mixed /
+// not known without counting.
+enum : int { TRI_FALSE = 0, TRI_TRUE = 1, TRI_MIXED = 2 };
+
+__device__ __forceinline__ int floor_div_i64(int64_t a, int64_t b) {
+    const int64_t q = a / b;
+    return (int)((a % b != 0 && a < 0) ? q - 1 : q);
+}
+
+__device__ __forceinline__ int pred_over_tile(int kind, int arg, int p0, int p1, int c0, int c1, int h) {
+    switch (kind) {
+    case PRED_CAUSAL:                                   // j <= p
+        return c1 <= p0 ? TRI_TRUE : (c0 > p1 ? TRI_FALSE : TRI_MIXED);
+    case PRED_WINDOW:                                   // p - j < arg
+        return (int64_t)p1 - c0 < arg ? TRI_TRUE : ((int64_t)p0 - c1 >= arg ? TRI_FALSE : TRI_MIXED);
+    case PRED_KV_LT:                                    // j < arg
+        return c1 < arg ? TRI_TRUE : (c0 >= arg ? TRI_FALSE : TRI_MIXED);
+    case PRED_CHUNK: {                                  // floor(p/arg) == floor(j/arg)
+        const int fp0 = floor_div_i64(p0, arg), fp1 = floor_div_i64(p1, arg);
+        const int fc0 = floor_div_i64(c0, arg), fc1 = floor_div_i64(c1, arg);
+        if (fp0 == fp1 && fc0 == fc1 && fp0 == fc0) return TRI_TRUE;
+        return (fp1 < fc0 || fc1 < fp0) ? TRI_FALSE : TRI_MIXED;
+    }
+    case PRED_STRIDE: return arg == 1 ? TRI_TRUE : TRI_MIXED;
+    case PRED_DOC: return TRI_MIXED;
+    default: return h < arg ? TRI_TRUE : TRI_FALSE;     // PRED_HEAD_LT
+    }
+}
+
+// Kleene AND over clauses of Kleene ORs: a tile is decided when the program is
+// true (false) on every cell; otherwise its cells are counted.
+__device__ __forceinline__ int program_over_tile(const MaskProgram& pg, int p0, int p1, int c0, int c1, int h) {
+    int all = TRI_TRUE;
+    for (int c = 0; c < pg.n_clauses; ++c) {
+        int any = TRI_FALSE;
+        for (int l = 0; l < pg.n_lits[c]; ++l) {
+            const int t = pred_over_tile(pg.kind[c][l], pg.arg[c][l], p0, p1, c0, c1, h);
+            if (t == TRI_TRUE) any = TRI_TRUE;
+            else if (t == TRI_MIXED && any == TRI_FALSE) any = TRI_MIXED;
+        }
+        if (any == TRI_FALSE) return TRI_FALSE;
+        if (any == TRI_MIXED) all = TRI_MIXED;
+    }
+    return all;
+}
+
 template <int KIND>
-__device__ __forceinline__ int corner_class(const MaskArgs& m, int p0, int p1, int c0, int c1, bool clipped) {
-    if constexpr (KIND == MASK_NOOP) {
+__device__ __forceinline__ int corner_class(const MaskArgs& m, int p0, int p1, int c0, int c1, bool clipped, int h) {
+    if constexpr (KIND == MASK_PROGRAM) {
+        const int t = program_over_tile(m.prog, p0, p1, c0, c1, h);
+        if (t == TRI_FALSE) return TILE_EMPTY;
+        if (t == TRI_TRUE) return clipped ? TILE_PARTIAL : TILE_FULL;
+        return TILE_COUNT;
+    } else if constexpr (KIND == MASK_NOOP) {
         return clipped ? TILE_PARTIAL : TILE_FULL;
     } else {
         if (c0 > p1) return TILE_EMPTY;                       // every kv > every q: causal part fails
@@ -72,7 +124,7 @@ __device__ __forceinline__ int class_of(const uint32_t* words, int kb) {
 // write the lists.
 template <int KIND>
 constexpr int build_threads() {
-    return (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL) ? 1024 : 128;
+    return (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL || KIND == MASK_PROGRAM) ? 1024 : 128;
 }
 constexpr int kCountBatch = 8;
 
@@ -94,7 +146,17 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
     const int64_t row_id = (int64_t)bh * a.nQB + qb;
     const int p0 = row0 + a.mask.q_offset, p1 = p0 + rows - 1;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if constexpr (KIND == MASK_DOC_CAUSAL) {
+    const int h = bh % a.Hm;   // query head of this mask row (0 when broadcast)
+    if constexpr (KIND == MASK_PROGRAM) {
+        if (!a.mask.uses_doc && threadIdx.x == 0) {
+            // one run holding every row, with no document
+            run_start[0] = 0;
+            run_start[1] = rows;
+            run_doc[0] = -2;
+            run_count = 1;
+        }
+    }
+    if (KIND == MASK_DOC_CAUSAL || (KIND == MASK_PROGRAM && a.mask.uses_doc)) {
         if (wave == 0) {
             int runs = 0;
             for (int i0 = 0; i0 < rows; i0 += 64) {
@@ -128,15 +190,15 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
             const int c0 = kb * a.kv_block;
             const int c1 = min(c0 + a.kv_block, a.S) - 1;
             const bool clipped = rows < a.q_block || c0 + a.kv_block > a.S;
-            word |= (uint32_t)corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped) << (2 * t);
+            word |= (uint32_t)corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped, h) << (2 * t);
         }
         tile_class[w] = word;
     }
     __syncthreads();
-    if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL) {
+    if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL || KIND == MASK_PROGRAM) {
         // A wave takes kCountBatch of its tiles at a time so that the column id
         // loads of the batch are in flight together.
-        const int runs = KIND == MASK_DOC_CAUSAL ? run_count : 0;
+        const int runs = (KIND == MASK_DOC_CAUSAL || KIND == MASK_PROGRAM) ? run_count : 0;
         for (int kb0 = wave; kb0 < a.nKB; kb0 += kBuildWaves * kCountBatch) {
             bool todo[kCountBatch];
             bool any = false;
@@ -153,7 +215,7 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
             for (int j0 = 0; j0 < a.kv_block; j0 += 64) {
                 const int jj = j0 + lane;
                 int doc_col[kCountBatch];
-                if constexpr (KIND == MASK_DOC_CAUSAL) {
+                if (KIND == MASK_DOC_CAUSAL || (KIND == MASK_PROGRAM && a.mask.uses_doc)) {
 #pragma unroll
                     for (int u = 0; u < kCountBatch; ++u) {
                         const int col = (kb0 + u * kBuildWaves) * a.kv_block + jj;
@@ -171,6 +233,14 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
                         // column by rows p < col + window
                         const int hi = (col < a.mask.sinks || a.mask.window > p1 - col) ? p1 : col + a.mask.window - 1;
                         count[u] += max(0, hi - lo + 1);
+                    } else if constexpr (KIND == MASK_PROGRAM) {
+                        // every row of every document run, evaluated cell by cell
+                        const int dc = a.mask.uses_doc ? doc_col[u] : -1;
+                        for (int r = 0; r < runs; ++r) {
+                            const int dp = run_doc[r];
+                            for (int p = p0 + run_start[r]; p < p0 + run_start[r + 1]; ++p)
+                                count[u] += program_holds(a.mask.prog, p, col, h, dp, dc) ? 1 : 0;
+                        }
                     } else {
                         // rows of a run with the column's document, at or after the column
                         for (int r = 0; r < runs; ++r) {
@@ -238,6 +308,7 @@ hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream) {
     case MASK_NOOP: return launch_build<MASK_NOOP>(a, stream);
     case MASK_CAUSAL: return launch_build<MASK_CAUSAL>(a, stream);
     case MASK_CAUSAL_WINDOW_SINKS: return launch_build<MASK_CAUSAL_WINDOW_SINKS>(a, stream);
+    case MASK_PROGRAM: return launch_build<MASK_PROGRAM>(a, stream);
     default: return launch_build<MASK_DOC_CAUSAL>(a, stream);
     }
 }

@@ -36,8 +36,29 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// True when a PROGRAM mask has a predicate of this kind.
+bool program_uses(const flex_mask_params* m, int pred) {
+    if (m->kind != FLEX_MASK_PROGRAM) return false;
+    for (int c = 0; c < m->n_clauses && c < FLEX_MAX_CLAUSES; ++c)
+        for (int l = 0; l < m->clause[c].n && l < FLEX_MAX_LITERALS; ++l)
+            if (m->clause[c].lit[l].kind == pred) return true;
+    return false;
+}
+
+// True when every visible cell has j <= p: the mask is causal-type (CAUSAL,
+// the causal window, DOC_CAUSAL, or a PROGRAM with a clause that is CAUSAL
+// alone).
+bool mask_implies_causal(const flex_mask_params* m) {
+    if (m->kind == FLEX_MASK_CAUSAL || m->kind == FLEX_MASK_CAUSAL_WINDOW_SINKS || m->kind == FLEX_MASK_DOC_CAUSAL)
+        return true;
+    if (m->kind != FLEX_MASK_PROGRAM) return false;
+    for (int c = 0; c < m->n_clauses; ++c)
+        if (m->clause[c].n == 1 && m->clause[c].lit[0].kind == FLEX_PRED_CAUSAL) return true;
+    return false;
+}
+
 flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
-    if (m->kind < FLEX_MASK_NOOP || m->kind > FLEX_MASK_DOC_CAUSAL)
+    if (m->kind < FLEX_MASK_NOOP || m->kind > FLEX_MASK_PROGRAM)
         return fail(FLEX_ERR_PARAM, "unknown mask kind %d", m->kind);
     if (m->q_offset <= -kMaxLen || m->q_offset >= kMaxLen || m->q_offset + L >= kMaxLen)
         return fail(FLEX_ERR_PARAM, "q_offset %lld out of range for L=%lld", (long long)m->q_offset, (long long)L);
@@ -45,9 +66,27 @@ flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
         if (m->window < 1) return fail(FLEX_ERR_PARAM, "window must be >= 1 (got %d)", m->window);
         if (m->sinks < 0) return fail(FLEX_ERR_PARAM, "sinks must be >= 0 (got %d)", m->sinks);
     }
-    if (m->kind == FLEX_MASK_DOC_CAUSAL) {
-        if (m->doc_id == nullptr) return fail(FLEX_ERR_NULL, "DOC_CAUSAL needs doc_id");
-        if (m->q_offset < 0) return fail(FLEX_ERR_PARAM, "DOC_CAUSAL needs q_offset >= 0");
+    if (m->kind == FLEX_MASK_PROGRAM) {
+        if (m->n_clauses < 1 || m->n_clauses > FLEX_MAX_CLAUSES)
+            return fail(FLEX_ERR_PARAM, "a mask program needs 1..%d clauses (got %d)", FLEX_MAX_CLAUSES, m->n_clauses);
+        for (int c = 0; c < m->n_clauses; ++c) {
+            const flex_mask_clause& cl = m->clause[c];
+            if (cl.n < 1 || cl.n > FLEX_MAX_LITERALS)
+                return fail(FLEX_ERR_PARAM, "clause %d needs 1..%d predicates (got %d)", c, FLEX_MAX_LITERALS, cl.n);
+            for (int l = 0; l < cl.n; ++l) {
+                const int kind = cl.lit[l].kind, arg = cl.lit[l].arg;
+                if (kind < FLEX_PRED_CAUSAL || kind > FLEX_PRED_HEAD_LT)
+                    return fail(FLEX_ERR_PARAM, "clause %d: unknown predicate kind %d", c, kind);
+                const bool positive = kind == FLEX_PRED_WINDOW || kind == FLEX_PRED_CHUNK || kind == FLEX_PRED_STRIDE;
+                const bool non_negative = kind == FLEX_PRED_KV_LT || kind == FLEX_PRED_HEAD_LT;
+                if ((positive && arg < 1) || (non_negative && arg < 0))
+                    return fail(FLEX_ERR_PARAM, "clause %d: predicate %d argument %d out of range", c, kind, arg);
+            }
+        }
+    }
+    if (m->kind == FLEX_MASK_DOC_CAUSAL || program_uses(m, FLEX_PRED_DOC)) {
+        if (m->doc_id == nullptr) return fail(FLEX_ERR_NULL, "a document mask needs doc_id");
+        if (m->q_offset < 0) return fail(FLEX_ERR_PARAM, "a document mask needs q_offset >= 0");
         const int64_t need = std::max<int64_t>(S, m->q_offset + L);
         if (m->doc_len < need || m->doc_len >= kMaxLen)
             return fail(FLEX_ERR_PARAM, "doc_len %lld must cover max(S, q_offset + L) = %lld",
@@ -59,13 +98,25 @@ flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
 }
 
 MaskArgs to_mask_args(const flex_mask_params* m) {
-    MaskArgs a;
+    MaskArgs a{};
     a.kind = m->kind;
     a.window = m->window;
     a.sinks = m->sinks;
     a.q_offset = (int)m->q_offset;
     a.doc_id = m->doc_id;
     a.doc_len = (int)std::min<int64_t>(m->doc_len, kMaxLen - 1);
+    a.uses_doc = (m->kind == FLEX_MASK_DOC_CAUSAL || program_uses(m, FLEX_PRED_DOC)) ? 1 : 0;
+    if (m->kind == FLEX_MASK_PROGRAM) {
+        a.prog.n_clauses = m->n_clauses;
+        for (int c = 0; c < m->n_clauses; ++c) {
+            a.prog.n_lits[c] = m->clause[c].n;
+            for (int l = 0; l < m->clause[c].n; ++l) {
+                a.prog.kind[c][l] = m->clause[c].lit[l].kind;
+                a.prog.arg[c][l] = m->clause[c].lit[l].arg;
+            }
+        }
+    }
+    if (!a.uses_doc) a.doc_len = 0;
     return a;
 }
 
@@ -184,13 +235,17 @@ static flex_status check_fwd(const void* q, const void* k, const void* v, int32_
     if (S * std::max(ks[2], (int64_t)D) * elem >= (int64_t(1) << 31) ||
         S * std::max(vs[2], (int64_t)D) * elem >= (int64_t(1) << 31))
         return fail(FLEX_ERR_UNSUPPORTED, "one K or V head slice (S x row stride) must stay below 2 GiB");
-    if (score->kind < FLEX_SCORE_NONE || score->kind > FLEX_SCORE_SOFTCAP_ALIBI)
+    if (score->kind < FLEX_SCORE_NONE || score->kind > FLEX_SCORE_ALIBI)
         return fail(FLEX_ERR_PARAM, "unknown score kind %d", score->kind);
-    if (score->kind != FLEX_SCORE_NONE && !(score->cap > 0.0f && std::isfinite(score->cap)))
+    const bool capped = score->kind == FLEX_SCORE_SOFTCAP || score->kind == FLEX_SCORE_SOFTCAP_ALIBI;
+    const bool alibi = score->kind == FLEX_SCORE_SOFTCAP_ALIBI || score->kind == FLEX_SCORE_ALIBI;
+    if (capped && !(score->cap > 0.0f && std::isfinite(score->cap)))
         return fail(FLEX_ERR_PARAM, "soft-cap needs a finite cap > 0");
-    if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI && !std::isfinite(score->alibi_m))
-        return fail(FLEX_ERR_PARAM, "alibi_m must be finite");
-    return check_mask(mask, L, S);
+    if (alibi && !std::isfinite(score->alibi_m)) return fail(FLEX_ERR_PARAM, "alibi_m must be finite");
+    if (flex_status s = check_mask(mask, L, S)) return s;
+    if (program_uses(mask, FLEX_PRED_HEAD_LT) && bm->H != Hq)
+        return fail(FLEX_ERR_BLOCKMASK, "the mask reads the query head: block mask H=%d must be Hq=%d", bm->H, Hq);
+    return FLEX_OK;
 }
 
 size_t flex_attn_fwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
@@ -206,11 +261,23 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
                           const int64_t k_strides[3], const int64_t v_strides[3], float scale,
                           const flex_score_params* score, const flex_mask_params* mask, const flex_block_mask* bm,
                           void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return flex_attn_fwd_aux(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, scale, score, mask,
+                             bm, out, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                              int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                              const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                              const flex_score_params* score, const flex_mask_params* mask,
+                              const flex_block_mask* bm, void* out, float* lse, float* max_scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
                                   bm, out, lse))
         return s;
     if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
+    if (max_scores && (reinterpret_cast<uintptr_t>(max_scores) & 3u))
+        return fail(FLEX_ERR_LAYOUT, "max_scores must be 4-byte aligned");
     const size_t need = attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block,
                                                  bm->num_kv_blocks, bm->B, bm->H);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -223,6 +290,7 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
     a.v = v;
     a.out = out;
     a.lse = lse;
+    a.max_scores = max_scores;
     a.q_sb = q_strides[0]; a.q_sh = q_strides[1]; a.q_sr = q_strides[2];
     a.k_sb = k_strides[0]; a.k_sh = k_strides[1]; a.k_sr = k_strides[2];
     a.v_sb = v_strides[0]; a.v_sh = v_strides[1]; a.v_sr = v_strides[2];
@@ -234,7 +302,8 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
     a.group = Hq / Hkv;
     a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
     a.score_kind = score->kind;
-    a.cap = score->kind == FLEX_SCORE_NONE ? 1.0f : score->cap;
+    const bool capped = score->kind == FLEX_SCORE_SOFTCAP || score->kind == FLEX_SCORE_SOFTCAP_ALIBI;
+    a.cap = capped ? score->cap : 1.0f;
     a.alibi_m = score->alibi_m;
     a.sc = score_consts(a.scale, a.cap, a.score_kind);
     a.mask = to_mask_args(mask);
@@ -254,11 +323,11 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
     // so the range [ref - 120, ref + 64] (base 2) loses nothing.
     a.ref_mode = 0;
     a.ref_fixed = 0.0f;
-    if (dtype == FLEX_BF16 && score->kind != FLEX_SCORE_NONE) {
+    if (dtype == FLEX_BF16 && capped && max_scores == nullptr) {
         const double c2 = (double)score->cap * 1.4426950408889634;
         bool ok = c2 <= 92.0;
         if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI)
-            ok = ok && mask->kind != FLEX_MASK_NOOP && mask->q_offset + L <= S;
+            ok = ok && mask_implies_causal(mask) && mask->q_offset + L <= S;
         if (ok) {
             a.ref_mode = 1;
             a.ref_fixed = (float)(c2 <= 63.0 ? c2 : 120.0 - c2);

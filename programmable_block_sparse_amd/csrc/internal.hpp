@@ -41,6 +41,7 @@ struct FwdArgs {
     const void* v;
     void* out;
     float* lse;
+    float* max_scores;   // optional row maxima of the visible scores (natural units)
     int64_t q_sb, q_sh, q_sr;
     int64_t k_sb, k_sh, k_sr;
     int64_t v_sb, v_sh, v_sr;
@@ -67,7 +68,7 @@ struct FwdArgs {
     int ksplit;
     // split-KV decode (splits == 0: prefill kernel)
     float* ws_acc;      // [splits][B][Hq][L][D] partial numerators
-    float* ws_ml;       // [splits][B][Hq][L][4]  partial (base-2 reference, sum p, sum rounded p, 0)
+    float* ws_ml;       // [splits][B][Hq][L][4]  partial (base-2 reference, sum p, sum rounded p, max score)
     int splits;
 };
 
@@ -80,6 +81,12 @@ int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D);
 ScoreConsts score_consts(float scale, float cap, int score_kind);
 
 int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, int kv_block, int nKB, int Hm);
+
+// Per dtype / head-dimension launchers (one translation unit each).
+hipError_t launch_attn_fwd_bf16_d64(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16_d128(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32_d64(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32_d128(const FwdArgs& a, hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for an unsupported
 // combination (the host validated the combination before).

@@ -184,6 +184,65 @@ def test_fp32_alignment_unit_is_four_elements(lib):
     assert f.call(lib) == LAYOUT
 
 
+def _program(*clauses, q_offset=0, doc=None, doc_len=0):
+    m = _mask("program", q_offset=q_offset, doc=doc, doc_len=doc_len)
+    m.n_clauses = len(clauses)
+    for i, c in enumerate(clauses):
+        m.clause[i].n = len(c)
+        for j, (name, arg) in enumerate(c):
+            m.clause[i].lit[j].kind = pbs.PREDICATES[name] if isinstance(name, str) else name
+            m.clause[i].lit[j].arg = arg
+    return m
+
+
+def test_program_mask_validation(lib):
+    L = S = 256
+    ok = _program([("causal", 0)], [("window", 64), ("kv_lt", 4)])
+    bm = _bm(L, S, 64, 64)
+    # valid programs pass validation and fail only at the (absent) GPU launch
+    assert build(lib, ok, L, S, bm) in (0, HIP)
+    assert build(lib, _program(), L, S, bm) == PARAM                                   # no clause
+    five = _program(*[[("causal", 0)]] * 4)
+    five.n_clauses = 5
+    assert build(lib, five, L, S, bm) == PARAM                                         # too many clauses
+    empty = _program([("causal", 0)])
+    empty.clause[0].n = 0
+    assert build(lib, empty, L, S, bm) == PARAM                                        # empty clause
+    three = _program([("causal", 0)])
+    three.clause[0].n = 3
+    assert build(lib, three, L, S, bm) == PARAM                                        # too many predicates
+    assert build(lib, _program([(9, 0)]), L, S, bm) == PARAM                           # unknown predicate
+    for name, arg in (("window", 0), ("chunk", 0), ("stride", 0), ("kv_lt", -1), ("head_lt", -2)):
+        assert build(lib, _program([(name, arg)]), L, S, bm) == PARAM, name
+    assert build(lib, _program([("doc", 0)]), L, S, bm) == NULL                        # doc predicate, no ids
+    assert build(lib, _program([("doc", 0)], doc=FAKE, doc_len=S - 1), L, S, bm) == PARAM
+    assert build(lib, _program([("doc", 0)], doc=FAKE, doc_len=S, q_offset=-1), L, S, bm) == PARAM
+
+
+def test_fwd_program_and_score_rules(lib):
+    f = Fwd()
+    f.mask = _program([("causal", 0)], [("head_lt", 2), ("window", 32)], q_offset=f.S - f.L)
+    assert f.call(lib) == BLOCKMASK                     # reads the head but the block mask is broadcast
+    assert "head" in pbs.flex_last_error()
+    f = Fwd()
+    f.score = _score("alibi", alibi_m=float("nan"))
+    assert f.call(lib) == PARAM
+    f = Fwd()
+    f.score = _score("alibi", cap=0.0)                   # no cap needed for the uncapped ALiBi
+    assert f.call(lib) in (0, HIP)
+
+
+def test_aux_entry_point_checks_max_scores_alignment(lib):
+    f = Fwd()
+    a3 = lambda x: (ctypes.c_int64 * 3)(*x)
+    call = lambda ms: lib.flex_attn_fwd_aux(f.q, f.k, f.v, f.dtype, f.B, f.Hq, f.Hkv, f.L, f.S, f.D, a3(f.qs),
+                                             a3(f.ks), a3(f.vs), ctypes.c_float(0.0), ctypes.byref(f.score),
+                                             ctypes.byref(f.mask), ctypes.byref(f.bm), f.out, f.lse, ms, None, 0,
+                                             None)
+    assert call(FAKE + 2) == LAYOUT
+    assert call(None) in (0, HIP)
+
+
 def test_workspace_query_rejects_bad_shapes(lib):
     bm = _bm(256, 256, 128, 64)
     assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 3, 256, 256, 64, ctypes.byref(bm)) == 0

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import programmable_block_sparse_amd as pbs
-from gpu_common import (assert_attention_close, assert_block_mask_equal, oracle_mods, require_gpu)
+from gpu_common import TOL_LSE, assert_attention_close, assert_block_mask_equal, oracle_mods, require_gpu
 from oracle import MaskMod, ScoreMod, attention, build_block_mask
 from workloads import (WORKLOAD_ORDER, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
                        workload_doc_ids)
@@ -28,9 +28,14 @@ def dev():
     return require_gpu()
 
 
-def _mask_pair(kind, window=0, sinks=0, q_offset=0, doc_np=None, doc_t=None):
-    return (pbs.MaskSpec(kind=kind, window=window, sinks=sinks, q_offset=q_offset, doc_id=doc_t),
-            MaskMod(kind, window=window, sinks=sinks, doc_id=doc_np))
+def _mask_pair(kind, window=0, sinks=0, q_offset=0, doc_np=None, doc_t=None, clauses=()):
+    clauses = tuple(tuple(c) for c in clauses)
+    return (pbs.MaskSpec(kind=kind, window=window, sinks=sinks, q_offset=q_offset, doc_id=doc_t, clauses=clauses),
+            MaskMod(kind, window=window, sinks=sinks, doc_id=doc_np, clauses=clauses))
+
+
+def _uses_doc(kind, clauses):
+    return kind == "doc_causal" or any(name == "doc" for c in clauses for name, _ in c)
 
 
 def _rand_doc(rng, n):
@@ -125,27 +130,42 @@ def _widen(x_f32, dtype):
 
 
 def run_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_kind, window=0, sinks=0,
-             q_offset=None, value_scale=1.0, scale=None, with_lse=True, what=""):
+             q_offset=None, value_scale=1.0, scale=None, with_lse=True, what="", clauses=(), bm_heads=1,
+             with_max=False):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32) * np.float32(value_scale)
     off = S - L if q_offset is None else q_offset
     doc_np = doc_t = None
-    if mask_kind == "doc_causal":
+    if _uses_doc(mask_kind, clauses):
         doc_np = _rand_doc(rng, max(S, off + L))
         doc_t = torch.from_numpy(doc_np).to(dev)
-    mspec, mmod = _mask_pair(mask_kind, window, sinks, off, doc_np, doc_t)
+    mspec, mmod = _mask_pair(mask_kind, window, sinks, off, doc_np, doc_t, clauses)
     sspec = pbs.ScoreSpec(**score)
     smod = ScoreMod(**score)
-    bm = pbs.flex_blockmask_build(mspec, L, S, qb, kb, device=dev)
-    out, lse = pbs.flex_attn_fwd(_tensor(q, dtype, dev), _tensor(k, dtype, dev), _tensor(v, dtype, dev),
-                                 block_mask=bm, score=sspec, mask=mspec, scale=scale, return_lse=with_lse)
+    bm = pbs.flex_blockmask_build(mspec, L, S, qb, kb, H=bm_heads, device=dev)
+    qt, kt, vt = _tensor(q, dtype, dev), _tensor(k, dtype, dev), _tensor(v, dtype, dev)
+    if with_max:
+        out, lse, mx = pbs.flex_attn_fwd_aux(qt, kt, vt, block_mask=bm, score=sspec, mask=mspec, scale=scale,
+                                             return_lse=with_lse)
+    else:
+        out, lse = pbs.flex_attn_fwd(qt, kt, vt, block_mask=bm, score=sspec, mask=mspec, scale=scale,
+                                     return_lse=with_lse)
     torch.cuda.synchronize()
     sc = pbs.default_scale(D) if scale is None else float(np.float32(scale))
-    out_ref, lse_ref = attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale=sc, score=smod,
-                                 mask=mmod, q_offset=off)
-    return assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
+    out_ref, lse_ref, mx_ref = attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale=sc,
+                                         score=smod, mask=mmod, q_offset=off, with_max=True)
+    err = assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
+    if with_max:
+        # the row maximum is a score like lse: same error sources, same bound
+        m = mx.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isneginf(m), np.isneginf(mx_ref)), f"{what}: -inf pattern of max_scores"
+        fin = ~np.isneginf(mx_ref)
+        merr = np.abs(m[fin] - mx_ref[fin]).max() if fin.any() else 0.0
+        print(f"[parity] {what}: max_scores max-abs {merr:.3e}")
+        assert merr <= TOL_LSE, f"{what}: max_scores max-abs {merr:.3e}"
+    return err
 
 
 SCORES = [dict(kind="none"), dict(kind="softcap", cap=5.0), dict(kind="softcap_alibi", cap=30.0, alibi_m=8.0)]
@@ -326,3 +346,109 @@ def test_run_to_run_bitwise_determinism(dev):
     o2, l2 = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------ program masks, plain ALiBi, max_scores
+# The tensorcad "Attention expressions" Examples (mask column) as programs:
+# an AND of clauses, each an OR of predicates (2kiu guide, section 4.3).
+PROGRAMS = {
+    "prefix_lm": ((("causal", 0), ("kv_lt", 16)),),
+    "sink_window": ((("causal", 0),), (("window", 40), ("kv_lt", 4))),
+    "chunked": ((("causal", 0),), (("chunk", 48),)),
+    "every_4th": ((("causal", 0),), (("stride", 4),)),
+    "half_heads_global": ((("causal", 0),), (("head_lt", 2), ("window", 30))),
+    "doc_window": ((("causal", 0),), (("doc", 0),), (("window", 90), ("kv_lt", 2))),
+}
+
+
+def _random_program(rng, with_head, with_doc):
+    names = ["causal", "window", "kv_lt", "chunk", "stride"] + (["head_lt"] if with_head else []) + \
+            (["doc"] if with_doc else [])
+    clauses = []
+    for _ in range(int(rng.integers(1, 5))):
+        lits = []
+        for _ in range(int(rng.integers(1, 3))):
+            n = str(rng.choice(names))
+            arg = {"causal": 0, "doc": 0, "window": int(rng.integers(1, 60)), "kv_lt": int(rng.integers(0, 40)),
+                   "chunk": int(rng.integers(1, 70)), "stride": int(rng.integers(1, 7)),
+                   "head_lt": int(rng.integers(0, 4))}[n]
+            lits.append((n, arg))
+        clauses.append(tuple(lits))
+    return tuple(clauses)
+
+
+def test_blockmask_program_fuzz_bit_exact(dev):
+    rng = np.random.default_rng(4321)
+    n = 0
+    for trial in range(90):
+        L, S = int(rng.integers(1, 260)), int(rng.integers(1, 260))
+        QB = int(rng.choice([1, 3, 16, 64, 128]))
+        KB = int(rng.choice([1, 5, 64, 128]))
+        with_doc = trial % 3 == 0
+        Hm = 3 if trial % 4 == 1 else 1
+        off = int(rng.integers(0, 30)) if with_doc else int(rng.integers(-40, 40))
+        clauses = _random_program(rng, Hm > 1, with_doc)
+        doc_np = doc_t = None
+        if with_doc:
+            doc_np = _rand_doc(rng, max(S, off + L) + int(rng.integers(0, 3)))
+            doc_t = torch.from_numpy(doc_np).to(dev)
+        spec, mod = _mask_pair("program", q_offset=off, doc_np=doc_np, doc_t=doc_t, clauses=clauses)
+        print(f"[blockmask] program {clauses} L={L} S={S} tiles={QB}x{KB} off={off} H={Hm}", flush=True)
+        gpu = pbs.flex_blockmask_build(spec, L, S, QB, KB, H=Hm, device=dev)
+        ref = build_block_mask(mod, L, S, QB, KB, H=Hm, q_offset=off)
+        assert_block_mask_equal(gpu, ref)
+        n += 1
+    assert n == 90
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_attention_program_masks(dev, dtype, D):
+    scores = [dict(kind="none"), dict(kind="softcap", cap=20.0), dict(kind="alibi", alibi_m=8.0)]
+    for i, (name, clauses) in enumerate(PROGRAMS.items()):
+        score = scores[i % len(scores)]
+        Hq, Hkv = 4, 2
+        bm_heads = Hq if any(n == "head_lt" for c in clauses for n, _ in c) else 1
+        L, S = (211, 211) if i % 2 == 0 else (150, 333)
+        run_case(dev, seed=500 + i, dtype=dtype, B=2, Hq=Hq, Hkv=Hkv, L=L, S=S, D=D, qb=128, kb=64, score=score,
+                 mask_kind="program", clauses=clauses, bm_heads=bm_heads,
+                 what=f"{dtype} D={D} {name} {score}")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 128)])
+def test_plain_alibi_score(dev, dtype, D):
+    for i, mask in enumerate(MASKS):
+        run_case(dev, seed=600 + i, dtype=dtype, B=1, Hq=8, Hkv=4, L=190, S=260, D=D, qb=64, kb=64,
+                 score=dict(kind="alibi", alibi_m=8.0), what=f"{dtype} D={D} alibi {mask}", **mask)
+
+
+def test_max_scores_output(dev):
+    cases = [
+        dict(dtype="bf16", D=64, score=dict(kind="softcap_alibi", cap=30.0), mask_kind="causal"),
+        dict(dtype="bf16", D=128, score=dict(kind="softcap", cap=50.0), mask_kind="causal_window_sinks",
+             window=40, sinks=3),
+        dict(dtype="bf16", D=64, score=dict(kind="none"), mask_kind="program", clauses=PROGRAMS["every_4th"]),
+        dict(dtype="f32", D=64, score=dict(kind="alibi"), mask_kind="doc_causal"),
+    ]
+    for i, c in enumerate(cases):
+        c = dict(c)
+        run_case(dev, seed=700 + i, B=2, Hq=4, Hkv=2, L=170, S=230, qb=128, kb=64, with_max=True,
+                 what=f"max_scores {c}", **c)
+    # rows with no visible key (L > S, bottom-right): max_scores = -inf there
+    run_case(dev, seed=710, dtype="bf16", B=1, Hq=2, Hkv=1, L=200, S=90, D=64, qb=64, kb=64,
+             score=dict(kind="softcap", cap=10.0), mask_kind="causal", with_max=True, what="max_scores empty rows")
+
+
+def test_decode_path_programs_alibi_and_max(dev):
+    cases = [
+        (dict(mask_kind="program", clauses=PROGRAMS["chunked"]), dict(kind="softcap", cap=50.0), False),
+        (dict(mask_kind="program", clauses=PROGRAMS["prefix_lm"]), dict(kind="alibi"), False),
+        (dict(mask_kind="causal"), dict(kind="softcap", cap=50.0), True),
+        (dict(mask_kind="program", clauses=PROGRAMS["doc_window"]), dict(kind="none"), True),
+    ]
+    for i, (mask, score, with_max) in enumerate(cases):
+        for D in (64, 128):
+            B, Hkv, G, qb, L, S = 2, 2, 4, 16, 16, 3100
+            probe = pbs.flex_blockmask_build(pbs.MaskSpec(kind="causal"), L, S, qb, 64, device=dev)
+            assert pbs.flex_attn_fwd_workspace_bytes(torch.bfloat16, B, G * Hkv, Hkv, L, S, D, probe) > 0
+            run_case(dev, seed=800 + i + D, dtype="bf16", B=B, Hq=G * Hkv, Hkv=Hkv, L=L, S=S, D=D, qb=qb, kb=64,
+                     score=score, with_max=with_max, what=f"decode D={D} {mask} {score} max={with_max}", **mask)

@@ -403,3 +403,121 @@ def test_gqa_equals_repeated_heads_and_sdpa():
     ref = F(*(torch.from_numpy(x) for x in (q, k, v)), enable_gqa=True)
     out, _ = _attn(q, k, v)
     assert np.abs(out - ref.numpy()).max() < 1e-12
+
+
+# ------------------------------------- the menu's program masks and plain ALiBi
+# tensorcad "Attention expressions", Examples table; 2kiu guide, section 4.3
+# (and_masks folds from all-true with &, or_masks from all-false with |).
+def _visible_counts(mask, L, S, q_offset=0, h=0):
+    q = np.arange(L)[:, None] + q_offset
+    kv = np.arange(S)[None, :]
+    return mask(0, h, q, kv).sum(axis=1)
+
+
+def test_prefix_lm_counts():
+    # causal off, "kv <= q or kv < 16": row q sees max(q + 1, 16) keys
+    m = MaskMod("program", clauses=((("causal", 0), ("kv_lt", 16)),))
+    L = S = 40
+    assert list(_visible_counts(m, L, S)) == [max(q + 1, 16) for q in range(L)]
+
+
+def test_chunked_counts():
+    # causal on, "floor(q / C) == floor(kv / C)": row q sees the keys of its own
+    # chunk up to itself, q mod C + 1 of them
+    C = 8
+    m = MaskMod("program", clauses=((("causal", 0),), (("chunk", C),)))
+    L = S = 50
+    assert list(_visible_counts(m, L, S)) == [q % C + 1 for q in range(L)]
+
+
+def test_every_fourth_key_counts():
+    # causal on, "(q - kv) % 4 == 0": keys q, q-4, ..., floor(q/4) + 1 of them
+    m = MaskMod("program", clauses=((("causal", 0),), (("stride", 4),)))
+    L = S = 37
+    assert list(_visible_counts(m, L, S)) == [q // 4 + 1 for q in range(L)]
+
+
+def test_half_heads_global_counts():
+    # causal on, "h < heads / 2 or q - kv < W" with 4 heads, W = 5
+    m = MaskMod("program", clauses=((("causal", 0),), (("head_lt", 2), ("window", 5))))
+    L = S = 30
+    for h in range(4):
+        want = [q + 1 if h < 2 else min(q + 1, 5) for q in range(L)]
+        assert list(_visible_counts(m, L, S, h=h)) == want, h
+
+
+def test_programs_reproduce_the_fixed_menu():
+    # and_masks(causal, or_masks(window, sinks)) is the causal window with sinks,
+    # and_masks(causal, doc) the document mask; both are pinned above
+    rng = np.random.default_rng(21)
+    doc = np.repeat(np.arange(5), rng.integers(1, 9, size=5)).astype(np.int32)
+    S = len(doc)
+    q = np.arange(-3, S)[:, None]
+    kv = np.arange(S)[None, :]
+    a = MaskMod("program", clauses=((("causal", 0),), (("window", 7), ("kv_lt", 3))))
+    b = MaskMod("causal_window_sinks", window=7, sinks=3)
+    assert (a(0, 0, q, kv) == b(0, 0, q, kv)).all()
+    c = MaskMod("program", clauses=((("causal", 0),), (("doc", 0),)), doc_id=doc)
+    d = MaskMod("doc_causal", doc_id=doc)
+    q = np.arange(S)[:, None]
+    assert (c(0, 0, q, kv) == d(0, 0, q, kv)).all()
+    # folding identities: no clause is all-true; a clause is the OR of its predicates
+    assert MaskMod("program", clauses=())(0, 0, q, kv).all()
+    one = MaskMod("program", clauses=((("causal", 0), ("kv_lt", 2)),))(0, 0, q, kv)
+    assert (one == ((kv <= q) | (kv < 2))).all()
+
+
+def test_negative_positions_floor_semantics():
+    # with a negative q_offset the chunk and stride predicates use floor division
+    # and a non-negative remainder (Python operators, as on the page)
+    m = MaskMod("program", clauses=((("chunk", 3),), (("stride", 2),)))
+    for p in range(-7, 7):
+        for j in range(0, 9):
+            want = (p // 3 == j // 3) and ((p - j) % 2 == 0)
+            assert bool(m(0, 0, np.array(p), np.array(j))) == want, (p, j)
+
+
+def test_uncapped_alibi_geometric_weights():
+    # tensorcad Examples, the ALiBi row without a cap: with q = 0 every score is
+    # 0, so the weights are r^(i - j), r = e^-slope (same closed form as above)
+    rng = np.random.default_rng(22)
+    L, D, H = 9, 4, 4
+    q = np.zeros((1, H, L, D))
+    k = rng.standard_normal((1, H, L, D))
+    v = rng.standard_normal((1, H, L, D))
+    out, lse = _attn(q, k, v, ScoreMod("alibi", alibi_m=8.0), MaskMod("causal"))
+    for h in range(H):
+        r = math.exp(-2.0 ** (-8.0 * (h + 1) / H))
+        for i in range(L):
+            w = np.array([r ** (i - j) for j in range(i + 1)])
+            assert abs(lse[0, h, i] - math.log((1 - r ** (i + 1)) / (1 - r))) < 1e-12
+            assert np.abs(out[0, h, i] - (w @ v[0, h, :i + 1]) / w.sum()).max() < 1e-12
+    # an uncapped score differs from a capped one once scores are large
+    q2 = rng.standard_normal((1, H, L, D)) * 6
+    a, _ = _attn(q2, k, v, ScoreMod("alibi"), MaskMod("causal"), scale=1.0)
+    b, _ = _attn(q2, k, v, ScoreMod("softcap_alibi", cap=1.0), MaskMod("causal"), scale=1.0)
+    assert np.abs(a - b).max() > 1e-3
+
+
+def test_max_scores_closed_forms():
+    # row maxima of the scores entering the softmax: with q = 0 and ALiBi the
+    # row's own key has bias 0 and every other visible key a negative one
+    rng = np.random.default_rng(23)
+    L, D, H = 8, 4, 2
+    q = np.zeros((1, H, L, D))
+    k = rng.standard_normal((1, H, L, D))
+    v = rng.standard_normal((1, H, L, D))
+    _, lse, mx = attention(q, k, v, scale=0.5, score=ScoreMod("alibi"), mask=MaskMod("causal"), q_offset=0,
+                           with_max=True)
+    assert np.abs(mx).max() == 0.0
+    assert (lse >= mx).all()
+    # rows that see no key have max -inf; plain scores: the max is the largest dot
+    q3 = rng.standard_normal((1, 1, 4, D))
+    k3 = rng.standard_normal((1, 1, 6, D))
+    v3 = rng.standard_normal((1, 1, 6, D))
+    _, _, mx3 = attention(q3, k3, v3, scale=1.0, score=ScoreMod(), mask=MaskMod("causal"), q_offset=-2,
+                          with_max=True)
+    dots = q3[0, 0] @ k3[0, 0].T
+    assert mx3[0, 0, 0] == -np.inf and mx3[0, 0, 1] == -np.inf
+    assert abs(mx3[0, 0, 2] - dots[2, 0]) < 1e-12
+    assert abs(mx3[0, 0, 3] - dots[3, :2].max()) < 1e-12
