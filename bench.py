@@ -255,7 +255,7 @@ def cpu_baseline(args, w, inp, out, lse, flops):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = None
-    mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"])
+    mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"], clauses=w.clauses)
     smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
     t0 = time.perf_counter()
     ref_bm = build_block_mask(mmod, w.L, w.S, w.q_block, w.kv_block, q_offset=w.q_offset)

@@ -23,6 +23,8 @@
 //
 // Layout conventions: cells beyond L or S are not visible; each index row
 // lists its tiles ascending, then the remaining tile indices ascending.
+#include <climits>
+
 #include "internal.hpp"
 
 namespace flexmi {
@@ -71,9 +73,13 @@ __device__ __forceinline__ int pred_over_tile(int kind, int arg, int p0, int p1,
 // true (false) on every cell; otherwise its cells are counted.
 __device__ __forceinline__ int program_over_tile(const MaskProgram& pg, int p0, int p1, int c0, int c1, int h) {
     int all = TRI_TRUE;
-    for (int c = 0; c < pg.n_clauses; ++c) {
+#pragma unroll
+    for (int c = 0; c < kMaxClauses; ++c) {
+        if (c >= pg.n_clauses) break;
         int any = TRI_FALSE;
-        for (int l = 0; l < pg.n_lits[c]; ++l) {
+#pragma unroll
+        for (int l = 0; l < kMaxLiterals; ++l) {
+            if (l >= pg.n_lits[c]) break;
             const int t = pred_over_tile(pg.kind[c][l], pg.arg[c][l], p0, p1, c0, c1, h);
             if (t == TRI_TRUE) any = TRI_TRUE;
             else if (t == TRI_MIXED && any == TRI_FALSE) any = TRI_MIXED;
@@ -82,6 +88,127 @@ __device__ __forceinline__ int program_over_tile(const MaskProgram& pg, int p0, 
         if (any == TRI_MIXED) all = TRI_MIXED;
     }
     return all;
+}
+
+// Visible cells of key column j over the block's rows, for a PROGRAM mask.
+// For a fixed column every predicate is an interval of positions p (causal:
+// p >= j; window: p <= j + W - 1; chunk: the chunk of j; kv_lt and head_lt:
+// everything or nothing), except stride (an interval plus p = j mod arg,
+// tracked incrementally) and doc (a per-run comparison).  The rows are then
+// scanned with compares only, run by run.
+__device__ __forceinline__ int count_program_column(const MaskProgram& pg, int j, int h, int doc_j, int p0,
+                                                    const int* run_start, const int* run_doc, int runs) {
+    constexpr int kInterval = 0, kStride = 1, kDoc = 2;
+    int lo[kMaxClauses][kMaxLiterals], hi[kMaxClauses][kMaxLiterals], kind[kMaxClauses][kMaxLiterals];
+    int modk[kMaxClauses][kMaxLiterals], res[kMaxClauses][kMaxLiterals];
+    const int p_first = p0 + run_start[0];
+#pragma unroll
+    for (int c = 0; c < kMaxClauses; ++c)
+#pragma unroll
+        for (int l = 0; l < kMaxLiterals; ++l) {
+            int L = INT_MIN, H = INT_MAX, K = kInterval, mk = 1, rs = 0;
+            if (c < pg.n_clauses && l < pg.n_lits[c]) {
+                const int arg = pg.arg[c][l];
+                switch (pg.kind[c][l]) {
+                case PRED_CAUSAL: L = j; break;
+                case PRED_WINDOW: H = (int)min<int64_t>((int64_t)j + arg - 1, INT_MAX); break;
+                case PRED_KV_LT: if (!(j < arg)) { L = 1; H = 0; } break;
+                case PRED_CHUNK: {
+                    const int64_t c0 = (int64_t)(j / arg) * arg;     // j >= 0
+                    L = (int)c0;
+                    H = (int)min<int64_t>(c0 + arg - 1, INT_MAX);
+                    break;
+                }
+                case PRED_STRIDE: {
+                    K = kStride;
+                    mk = arg;
+                    int r = (int)(((int64_t)p_first - j) % arg);
+                    rs = r < 0 ? r + arg : r;                        // (p - j) mod arg at the first row
+                    break;
+                }
+                case PRED_DOC: K = kDoc; break;
+                default: if (!(h < arg)) { L = 1; H = 0; } break;   // PRED_HEAD_LT
+                }
+            }
+            lo[c][l] = L; hi[c][l] = H; kind[c][l] = K; modk[c][l] = mk; res[c][l] = rs;
+        }
+    bool has_stride = false;
+#pragma unroll
+    for (int c = 0; c < kMaxClauses; ++c)
+#pragma unroll
+        for (int l = 0; l < kMaxLiterals; ++l) has_stride = has_stride || kind[c][l] == kStride;
+    // program value at position p of a run whose document equality is same_doc
+    auto holds = [&](int p, bool same_doc) {
+        bool all = true;
+#pragma unroll
+        for (int c = 0; c < kMaxClauses; ++c) {
+            if (c >= pg.n_clauses) break;
+            bool any = false;
+#pragma unroll
+            for (int l = 0; l < kMaxLiterals; ++l) {
+                if (l >= pg.n_lits[c]) break;
+                bool v = p >= lo[c][l] && p <= hi[c][l];
+                if (kind[c][l] == kDoc) v = v && same_doc;
+                any = any || v;
+            }
+            all = all && any;
+        }
+        return all;
+    };
+    int count = 0;
+    if (!has_stride && runs <= 8) {
+        // Without stride predicates the program is constant between interval
+        // end points, so each run is cut at those points and each piece is
+        // evaluated once.
+        for (int r = 0; r < runs; ++r) {
+            const bool same_doc = run_doc[r] == doc_j;
+            const int a0 = p0 + run_start[r], a1 = p0 + run_start[r + 1];   // [a0, a1)
+            int b = a0;
+            while (b < a1) {
+                int next = a1;   // smallest boundary above b
+#pragma unroll
+                for (int c = 0; c < kMaxClauses; ++c)
+#pragma unroll
+                    for (int l = 0; l < kMaxLiterals; ++l) {
+                        const int e0 = lo[c][l];
+                        const int64_t e1 = (int64_t)hi[c][l] + 1;
+                        if (e0 > b && e0 < next) next = e0;
+                        if (e1 > b && e1 < next) next = (int)e1;
+                    }
+                if (holds(b, same_doc)) count += next - b;
+                b = next;
+            }
+        }
+        return count;
+    }
+    for (int r = 0; r < runs; ++r) {
+        const int dp = run_doc[r];
+        const bool same_doc = dp == doc_j;
+        for (int p = p0 + run_start[r]; p < p0 + run_start[r + 1]; ++p) {
+            bool all = true;
+#pragma unroll
+            for (int c = 0; c < kMaxClauses; ++c) {
+                if (c >= pg.n_clauses) break;
+                bool any = false;
+#pragma unroll
+                for (int l = 0; l < kMaxLiterals; ++l) {
+                    if (l >= pg.n_lits[c]) break;
+                    bool v = p >= lo[c][l] && p <= hi[c][l];
+                    if (kind[c][l] == kStride) v = v && res[c][l] == 0;
+                    else if (kind[c][l] == kDoc) v = v && same_doc;
+                    any = any || v;
+                }
+                all = all && any;
+            }
+            count += all ? 1 : 0;
+#pragma unroll
+            for (int c = 0; c < kMaxClauses; ++c)
+#pragma unroll
+                for (int l = 0; l < kMaxLiterals; ++l)
+                    if (kind[c][l] == kStride && ++res[c][l] == modk[c][l]) res[c][l] = 0;
+        }
+    }
+    return count;
 }
 
 template <int KIND>
@@ -234,13 +361,8 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
                         const int hi = (col < a.mask.sinks || a.mask.window > p1 - col) ? p1 : col + a.mask.window - 1;
                         count[u] += max(0, hi - lo + 1);
                     } else if constexpr (KIND == MASK_PROGRAM) {
-                        // every row of every document run, evaluated cell by cell
                         const int dc = a.mask.uses_doc ? doc_col[u] : -1;
-                        for (int r = 0; r < runs; ++r) {
-                            const int dp = run_doc[r];
-                            for (int p = p0 + run_start[r]; p < p0 + run_start[r + 1]; ++p)
-                                count[u] += program_holds(a.mask.prog, p, col, h, dp, dc) ? 1 : 0;
-                        }
+                        count[u] += count_program_column(a.mask.prog, col, h, dc, p0, run_start, run_doc, runs);
                     } else {
                         // rows of a run with the column's document, at or after the column
                         for (int r = 0; r < runs; ++r) {

@@ -77,11 +77,19 @@ __device__ __forceinline__ bool pred_holds(int kind, int arg, int p, int j, int 
     }
 }
 
+// (Loops run over the fixed maxima with early exits so that every index is a
+// compile-time constant and the program stays in scalar registers.)
 __device__ __forceinline__ bool program_holds(const MaskProgram& pg, int p, int j, int h, int doc_p, int doc_j) {
     bool all = true;
-    for (int c = 0; c < pg.n_clauses; ++c) {
+#pragma unroll
+    for (int c = 0; c < kMaxClauses; ++c) {
+        if (c >= pg.n_clauses) break;
         bool any = false;
-        for (int l = 0; l < pg.n_lits[c]; ++l) any = any || pred_holds(pg.kind[c][l], pg.arg[c][l], p, j, h, doc_p, doc_j);
+#pragma unroll
+        for (int l = 0; l < kMaxLiterals; ++l) {
+            if (l >= pg.n_lits[c]) break;
+            any = any || pred_holds(pg.kind[c][l], pg.arg[c][l], p, j, h, doc_p, doc_j);
+        }
         all = all && any;
     }
     return all;

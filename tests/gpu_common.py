@@ -16,7 +16,7 @@ def require_gpu():
 
 
 def oracle_mods(w, doc_id=None):
-    return (MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=doc_id),
+    return (MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=doc_id, clauses=w.clauses),
             ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m))
 
 

@@ -16,7 +16,7 @@ import torch
 import programmable_block_sparse_amd as pbs
 from gpu_common import TOL_LSE, assert_attention_close, assert_block_mask_equal, oracle_mods, require_gpu
 from oracle import MaskMod, ScoreMod, attention, build_block_mask
-from workloads import (WORKLOAD_ORDER, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
+from workloads import (EXTRA_WORKLOADS, WORKLOAD_ORDER, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
                        workload_doc_ids)
 from workloads.torch_io import specs, to_device
 
@@ -106,13 +106,13 @@ def test_blockmask_extreme_parameters(dev):
     assert n == 45
 
 
-@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", WORKLOAD_ORDER + EXTRA_WORKLOADS)
 def test_blockmask_workloads_bit_exact(dev, name):
     w = WORKLOADS[name]
     doc_np = workload_doc_ids(w)
     doc_t = torch.from_numpy(doc_np).to(dev) if doc_np is not None else None
     spec, _ = specs(w, doc_t)
-    mod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=doc_np)
+    mod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=doc_np, clauses=w.clauses)
     gpu = pbs.flex_blockmask_build(spec, w.L, w.S, w.q_block, w.kv_block, device=dev)
     ref = build_block_mask(mod, w.L, w.S, w.q_block, w.kv_block, q_offset=w.q_offset)
     assert_block_mask_equal(gpu, ref)
@@ -308,7 +308,7 @@ def _sample_rows(w: Workload, rng, n_random=48):
     return np.array(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+@pytest.mark.parametrize("name", WORKLOAD_ORDER + EXTRA_WORKLOADS)
 def test_workload_parity_sampled(dev, name):
     w = WORKLOADS[name]
     inp = make_inputs(w)

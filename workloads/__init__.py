@@ -29,6 +29,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "draw_doc_lengths", "doc_ids_from_lengths",
     "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits", "make_inputs", "workload_doc_ids", "WORKLOAD_ORDER",
+    "EXTRA_WORKLOADS",
 ]
 
 
@@ -90,8 +91,8 @@ class Workload:
     S: int
     D: int
     dtype: str                  # "f32" or "bf16"
-    mask: str                   # "noop" | "causal" | "causal_window_sinks" | "doc_causal"
-    score: str                  # "none" | "softcap" | "softcap_alibi"
+    mask: str                   # "noop" | "causal" | "causal_window_sinks" | "doc_causal" | "program"
+    score: str                  # "none" | "softcap" | "softcap_alibi" | "alibi"
     q_block: int
     kv_block: int
     cap: float = 0.0
@@ -99,6 +100,7 @@ class Workload:
     window: int = 0
     sinks: int = 0
     docs: bool = False          # packed documents: draw lengths first
+    clauses: tuple = ()         # "program" masks: AND of clauses, each an OR of (predicate, arg)
 
     @property
     def q_offset(self) -> int:
@@ -116,8 +118,15 @@ WORKLOADS = {
                                  "causal_window_sinks", "softcap", 128, 64, cap=50.0, window=1024, sinks=4),
     "decode_verify": Workload("decode_verify", 5, 16, 32, 8, 16, 32768, 128, "bf16", "causal", "softcap",
                               16, 64, cap=50.0),
+    # mask programs from the tensorcad "Attention expressions" Examples table
+    "prefix_lm_alibi": Workload("prefix_lm_alibi", 6, 4, 16, 16, 2048, 2048, 64, "bf16", "program", "alibi",
+                                128, 64, clauses=((("causal", 0), ("kv_lt", 512)),)),
+    "chunked_gqa": Workload("chunked_gqa", 7, 2, 32, 8, 8192, 8192, 128, "bf16", "program", "none", 128, 64,
+                            clauses=((("causal", 0),), (("chunk", 2048),))),
 }
 WORKLOAD_ORDER = ["causal_f32", "causal_softcap_alibi", "doc_causal", "window_sinks_gqa", "decode_verify"]
+# the same parity tests cover these; they are measured apart from the five above
+EXTRA_WORKLOADS = ["prefix_lm_alibi", "chunked_gqa"]
 
 
 def get_workload(name: str) -> Workload:

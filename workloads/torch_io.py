@@ -27,7 +27,8 @@ def to_device(w: Workload, inputs: dict, device="cuda"):
 def specs(w: Workload, doc_id=None):
     """(MaskSpec, ScoreSpec) of the binding for this workload."""
     from programmable_block_sparse_amd import MaskSpec, ScoreSpec
-    mask = MaskSpec(kind=w.mask, window=w.window, sinks=w.sinks, q_offset=w.q_offset, doc_id=doc_id)
+    mask = MaskSpec(kind=w.mask, window=w.window, sinks=w.sinks, q_offset=w.q_offset, doc_id=doc_id,
+                    clauses=w.clauses)
     score = ScoreSpec(kind=w.score, cap=w.cap, alibi_m=w.alibi_m)
     return mask, score
 
