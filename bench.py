@@ -48,6 +48,11 @@ def parse():
 # Kernel sources whose code the HBM traffic figures under profiles/ were taken
 # on; a figure is reported only while these files are unchanged.
 KERNEL_SOURCES = ("programmable_block_sparse_amd/csrc/attn_fwd.hip",
+                  "programmable_block_sparse_amd/csrc/attn_fwd_impl.hpp",
+                  "programmable_block_sparse_amd/csrc/attn_fwd_bf16_d64.hip",
+                  "programmable_block_sparse_amd/csrc/attn_fwd_bf16_d128.hip",
+                  "programmable_block_sparse_amd/csrc/attn_fwd_f32_d64.hip",
+                  "programmable_block_sparse_amd/csrc/attn_fwd_f32_d128.hip",
                   "programmable_block_sparse_amd/csrc/device_common.hpp",
                   "programmable_block_sparse_amd/csrc/internal.hpp")
 
