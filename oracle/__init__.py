@@ -12,10 +12,11 @@ Contents
               -inf mask, then a row softmax (also how the pages describe the
               unfused fallback)
   blockmask   tile classification by counting visible cells, ordered lists,
-              to_dense / sparsity helpers
+              to_dense / sparsity helpers, the Q-side (transposed) lists
   blockwise   a second, independent float64 oracle that walks only the block
               lists with an online softmax; used to show the block mask loses
               nothing
+  backward    the gradients dq, dk, dv of the same definition
 
 Every function is pinned by tests under ``tests/`` that check it against
 printed worked examples, closed forms and brute force (none of them re-types
@@ -24,10 +25,12 @@ only say must be checked separately.
 """
 from .mods import ScoreMod, MaskMod, alibi_slope
 from .attention import attention, attention_rows
-from .blockmask import build_block_mask, to_dense, sparsity, visible_cells
+from .blockmask import build_block_mask, to_dense, sparsity, visible_cells, transpose_block_mask
 from .blockwise import blockwise_attention
+from .backward import attention_backward, score_derivative
 
 __all__ = [
     "ScoreMod", "MaskMod", "alibi_slope", "attention", "attention_rows",
     "build_block_mask", "to_dense", "sparsity", "visible_cells", "blockwise_attention",
+    "transpose_block_mask", "attention_backward", "score_derivative",
 ]

@@ -1,0 +1,78 @@
+"""Dense float64 gradients of masked, score-modified attention (test oracle).
+
+The forward is the definition the ``attention`` oracle follows: s = scale *
+q.k, z = g(s) where the mask holds and -inf elsewhere, P = row softmax of z,
+O = P V.  The pages say only that gradients flow through that same
+definition: the charlestar blog "FlexAttention score_mod / BlockMask" runs its
+windowed, soft-capped example and then calls backward on the summed output;
+the 2kiu "PyTorch Flex Attention complete guide" (section 3.3) derives a
+Q-side copy of the block lists for that pass, and its section 5.2 gives the
+backward its own tile sizes.  The formulas below are the chain rule through
+that definition, not anything printed on the pages:
+
+  dV_j  = sum_i P_ij dO_i
+  dP_ij = dO_i . V_j
+  D_i   = sum_j P_ij dP_ij            (= dO_i . O_i)
+  dZ_ij = P_ij (dP_ij - D_i)
+  dS_ij = dZ_ij * g'(s_ij) * scale    (g' = 1 - tanh(s/c)^2 under a soft-cap,
+                                       1 otherwise; the distance bias does not
+                                       depend on s)
+  dQ_i  = sum_j dS_ij K_j,   dK_j = sum_i dS_ij Q_i
+
+Under GQA the K/V gradients of a K/V head sum over its query heads.  Rows
+with no visible key have P = 0 and contribute nothing.  Nothing is blocked:
+each (batch, head) forms the full score matrix.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .mods import ScoreMod, MaskMod, SOFTCAP, SOFTCAP_ALIBI
+
+
+def score_derivative(score: ScoreMod, s):
+    """dg/ds for the menu (the bias term of the ALiBi kinds does not depend on s)."""
+    s = np.asarray(s, dtype=np.float64)
+    if score.kind in (SOFTCAP, SOFTCAP_ALIBI):
+        t = np.tanh(s / float(score.cap))
+        return 1.0 - t * t
+    return np.ones_like(s)
+
+
+def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int):
+    """(dq, dk, dv) in float64 for (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    q_pos = (np.arange(L, dtype=np.int64) + int(q_offset))[:, None]
+    kv = np.arange(S, dtype=np.int64)[None, :]
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            K, V = k[b, hk], v[b, hk]
+            s = (q[b, h] @ K.T) * float(scale)
+            vis = mask(b, h, q_pos, kv)
+            z = np.where(vis, score(s, b, h, q_pos, kv, Hq), -np.inf)
+            live = vis.any(axis=1)
+            P = np.zeros_like(z)
+            if live.any():
+                zl = z[live]
+                e = np.exp(zl - zl.max(axis=1, keepdims=True))
+                P[live] = e / e.sum(axis=1, keepdims=True)
+            O = P @ V
+            dO = dout[b, h]
+            dP = dO @ V.T
+            Dr = (dO * O).sum(axis=1, keepdims=True)
+            dZ = P * (dP - Dr)
+            dS = dZ * score_derivative(score, s) * float(scale)
+            dq[b, h] = dS @ K
+            dk[b, hk] += dS.T @ q[b, h]
+            dv[b, hk] += P.T @ dO
+    return dq, dk, dv

@@ -113,3 +113,33 @@ def tile_classes(bm: dict) -> np.ndarray:
                     for t in range(bm[num][b, h, r]):
                         cls[b, h, r, bm[ind][b, h, r, t]] = tag
     return cls
+
+
+def transpose_block_mask(bm: dict) -> dict:
+    """Q-side lists of a BlockMask: for every KV block, the Q blocks that list it.
+
+    The 2kiu guide, section 3.3, says from_kv_blocks derives the Q-side block
+    information from the KV-side lists by transposing them (for the backward
+    pass).  Read here as: q_num_blocks[b, h, kb] counts the rows qb whose
+    partial list holds kb, q_indices[b, h, kb] gives those qb ascending and then
+    the remaining Q-block indices ascending; full_q_* do the same for the full
+    lists.  Arrays are int32 of shapes (B, H, nKB) and (B, H, nKB, nQB).
+    """
+    B, H, nQB, nKB = bm["kv_indices"].shape
+    out = {}
+    for num, ind, tnum, tind in (("kv_num_blocks", "kv_indices", "q_num_blocks", "q_indices"),
+                                 ("full_kv_num_blocks", "full_kv_indices", "full_q_num_blocks", "full_q_indices")):
+        member = np.zeros((B, H, nKB, nQB), dtype=bool)
+        for b in range(B):
+            for h in range(H):
+                for qb in range(nQB):
+                    for t in range(bm[num][b, h, qb]):
+                        member[b, h, bm[ind][b, h, qb, t], qb] = True
+        cnt = np.zeros((B, H, nKB), dtype=np.int32)
+        idx = np.zeros((B, H, nKB, nQB), dtype=np.int32)
+        for b in range(B):
+            for h in range(H):
+                for kb in range(nKB):
+                    cnt[b, h, kb], idx[b, h, kb] = _ordered(member[b, h, kb])
+        out[tnum], out[tind] = cnt, idx
+    return out
