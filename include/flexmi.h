@@ -2,7 +2,7 @@
  * flexmi.h -- C ABI of the MI355X (gfx950) block-sparse attention library.
  *
  * The library computes the forward pass of programmable block-sparse attention
- * (the FlexAttention formulation):
+ * (the FlexAttention formulation) and its gradients:
  *
  *   s_ij  = scale * q_i . k_j
  *   z_ij  = g(s_ij, b, h, p_i, j)   if M(b, h, p_i, j)        else -inf
@@ -256,6 +256,77 @@ flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32
                               const flex_score_params* score, const flex_mask_params* mask,
                               const flex_block_mask* bm, void* out, float* lse, float* max_scores,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Q-side (transposed) BlockMask, used by the backward pass.  For every KV
+ * block it lists the Q blocks whose tile with it is partial, then (separately)
+ * full: the column view of the same tiles (2kiu guide, section 3.3:
+ * from_kv_blocks derives Q-side block information by transposing the KV-side
+ * lists).  Dims as in flex_block_mask.  Device arrays, int32, C order:
+ *   q_num_blocks       [B][H][num_kv_blocks]   number of partial tiles per column
+ *   q_indices          [B][H][num_kv_blocks][num_q_blocks]
+ *                      the partial tiles' Q-block indices ascending, then the
+ *                      remaining indices ascending
+ *   full_q_num_blocks  same shape as q_num_blocks, full tiles
+ *   full_q_indices     same layout as q_indices, full tiles */
+typedef struct {
+    int32_t B, H;
+    int32_t q_block, kv_block;
+    int32_t num_q_blocks, num_kv_blocks;
+    int32_t* q_num_blocks;
+    int32_t* q_indices;
+    int32_t* full_q_num_blocks;
+    int32_t* full_q_indices;
+} flex_block_mask_q;
+
+/* Fill the Q-side lists of a BlockMask (see flex_block_mask_q).
+ *   bm    a BlockMask as flex_blockmask_build writes it: the first
+ *         kv_num_blocks entries of each kv_indices row ascending (likewise the
+ *         full lists); counts are clamped to [0, num_kv_blocks] and a KV block
+ *         listed as both partial and full counts as partial
+ *   bmq   dims equal to bm's and the four caller-allocated device arrays, all
+ *         written by this call
+ * Errors: NULL, BLOCKMASK (dims differ or out of range), HIP. */
+flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block_mask_q* bmq, void* stream);
+
+/* Bytes of device workspace flex_attn_bwd needs: per (batch, query head, row,
+ * rows padded to a multiple of 64) the base-2 lse and D_i = dO_i . O_i, as
+ * float32.  Returns 0 for non-positive sizes. */
+size_t flex_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int64_t L);
+
+/* Block-sparse attention backward: the gradients of sum(out * dout) with
+ * respect to q, k and v for the forward of flex_attn_fwd (the charlestar blog
+ * "FlexAttention score_mod / BlockMask" runs its example and then calls
+ * backward on the summed output; the gradients are the chain rule through the
+ * forward definition at the top of this file):
+ *   P = exp(z - lse),  D_i = dout_i . out_i,
+ *   dS = P (dout v^T - D) g'(s) scale,
+ *   dq = dS k,  dk = dS^T q,  dv = P^T dout
+ * where g' = 1 - tanh(s / cap)^2 for the soft-cap kinds and 1 otherwise; under
+ * GQA dk and dv of a K/V head sum over its query heads.
+ *   q, k, v, dtype, B, Hq, Hkv, L, S, D, strides, scale, score, mask
+ *                as for the flex_attn_fwd call that produced out and lse
+ *   out, dout    device (B,Hq,L,D) contiguous, dtype `dtype`: the forward
+ *                output and the gradient flowing into it
+ *   lse          device float32 (B,Hq,L) contiguous from that forward call
+ *                (-inf rows, which saw no key, receive zero gradients)
+ *   bm, bmq      the BlockMask of that call and its Q-side lists
+ *                (flex_blockmask_transpose); q_block 64 or 128, kv_block a
+ *                multiple of 64
+ *   dq           device (B,Hq,L,D) contiguous, dtype `dtype`
+ *   dk, dv       device (B,Hkv,S,D) contiguous, dtype `dtype`
+ *   workspace    device scratch of at least flex_attn_bwd_workspace_bytes(),
+ *                16-byte aligned
+ * Every output element is written exactly once (no atomics), so results do
+ * not depend on scheduling.  bf16 outputs are rounded to nearest even from
+ * float32 accumulators.
+ * Errors: NULL, SHAPE, GQA, BLOCKMASK, UNSUPPORTED, LAYOUT, WORKSPACE, PARAM,
+ * HIP. */
+flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L,
+                          int64_t S, int32_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                          const int64_t v_strides[3], float scale, const flex_score_params* score,
+                          const flex_mask_params* mask, const flex_block_mask* bm, const flex_block_mask_q* bmq,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* flex_status_string(int32_t status);

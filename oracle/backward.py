@@ -39,8 +39,12 @@ def score_derivative(score: ScoreMod, s):
     return np.ones_like(s)
 
 
-def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int):
-    """(dq, dk, dv) in float64 for (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values."""
+def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int, pairs=None):
+    """(dq, dk, dv) in float64 for (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values.
+
+    ``pairs``: optional list of (batch, query head) to include; the gradients
+    then hold only those heads' terms (the others stay zero).  Default: all.
+    """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -53,26 +57,27 @@ def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: Ma
     dv = np.zeros_like(v)
     q_pos = (np.arange(L, dtype=np.int64) + int(q_offset))[:, None]
     kv = np.arange(S, dtype=np.int64)[None, :]
-    for b in range(B):
-        for h in range(Hq):
-            hk = h // group
-            K, V = k[b, hk], v[b, hk]
-            s = (q[b, h] @ K.T) * float(scale)
-            vis = mask(b, h, q_pos, kv)
-            z = np.where(vis, score(s, b, h, q_pos, kv, Hq), -np.inf)
-            live = vis.any(axis=1)
-            P = np.zeros_like(z)
-            if live.any():
-                zl = z[live]
-                e = np.exp(zl - zl.max(axis=1, keepdims=True))
-                P[live] = e / e.sum(axis=1, keepdims=True)
-            O = P @ V
-            dO = dout[b, h]
-            dP = dO @ V.T
-            Dr = (dO * O).sum(axis=1, keepdims=True)
-            dZ = P * (dP - Dr)
-            dS = dZ * score_derivative(score, s) * float(scale)
-            dq[b, h] = dS @ K
-            dk[b, hk] += dS.T @ q[b, h]
-            dv[b, hk] += P.T @ dO
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    for b, h in pairs:
+        hk = h // group
+        K, V = k[b, hk], v[b, hk]
+        s = (q[b, h] @ K.T) * float(scale)
+        vis = mask(b, h, q_pos, kv)
+        z = np.where(vis, score(s, b, h, q_pos, kv, Hq), -np.inf)
+        live = vis.any(axis=1)
+        P = np.zeros_like(z)
+        if live.any():
+            zl = z[live]
+            e = np.exp(zl - zl.max(axis=1, keepdims=True))
+            P[live] = e / e.sum(axis=1, keepdims=True)
+        O = P @ V
+        dO = dout[b, h]
+        dP = dO @ V.T
+        Dr = (dO * O).sum(axis=1, keepdims=True)
+        dZ = P * (dP - Dr)
+        dS = dZ * score_derivative(score, s) * float(scale)
+        dq[b, h] = dS @ K
+        dk[b, hk] += dS.T @ q[b, h]
+        dv[b, hk] += P.T @ dO
     return dq, dk, dv

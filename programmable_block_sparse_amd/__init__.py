@@ -1,4 +1,4 @@
-"""Python binding of libflexmi (MI355X block-sparse attention forward).
+"""Python binding of libflexmi (MI355X block-sparse attention, forward and backward).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI in ``include/flexmi.h``.  torch supplies device
@@ -9,6 +9,9 @@ the same names:
   flex_attn_fwd(q, k, v, score=..., mask=..., block_mask=..., ...) -> (out, lse)
   flex_attn_fwd_aux(q, k, v, ...) -> (out, lse, max_scores)
   flex_attn_fwd_workspace_bytes(...)
+  flex_blockmask_transpose(block_mask) -> BlockMaskQ
+  flex_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
+  flex_attn_bwd_workspace_bytes(B, Hq, L)
   flex_status_string(code)
 
 There is no fallback: if the native library is missing or cannot load, every
@@ -27,6 +30,7 @@ import torch  # imported first so the library binds to torch's HIP runtime
 __all__ = [
     "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
     "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_aux", "flex_attn_fwd_workspace_bytes",
+    "BlockMaskQ", "flex_blockmask_transpose", "flex_attn_bwd", "flex_attn_bwd_workspace_bytes",
     "flex_status_string", "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "PREDICATES", "EXPORTED_SYMBOLS",
 ]
 
@@ -37,6 +41,7 @@ PREDICATES = {"causal": 0, "window": 1, "kv_lt": 2, "chunk": 3, "stride": 4, "do
 MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
+                    "flex_blockmask_transpose", "flex_attn_bwd_workspace_bytes", "flex_attn_bwd",
                     "flex_status_string", "flex_last_error")
 
 
@@ -64,6 +69,13 @@ class flex_block_mask(ctypes.Structure):
                 ("kv_block", ctypes.c_int32), ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
                 ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
                 ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+
+
+class flex_block_mask_q(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("q_block", ctypes.c_int32),
+                ("kv_block", ctypes.c_int32), ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
+                ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
+                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -98,6 +110,15 @@ def load_library():
                                       ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask), P, P, P,
                                       P, ctypes.c_size_t, P]
     lib.flex_attn_fwd_aux.restype = ctypes.c_int
+    lib.flex_blockmask_transpose.argtypes = [ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P]
+    lib.flex_blockmask_transpose.restype = ctypes.c_int
+    lib.flex_attn_bwd_workspace_bytes.argtypes = [I32, I32, I64]
+    lib.flex_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.flex_attn_bwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3,
+                                  ctypes.c_float, ctypes.POINTER(flex_score_params), ctypes.POINTER(flex_mask_params),
+                                  ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P, P, P, P,
+                                  ctypes.c_size_t, P]
+    lib.flex_attn_bwd.restype = ctypes.c_int
     lib.flex_status_string.argtypes = [I32]
     lib.flex_status_string.restype = ctypes.c_char_p
     lib.flex_last_error.argtypes = []
@@ -326,6 +347,100 @@ def _fwd(q, k, v, block_mask, score, mask, scale, return_lse, return_max, out, l
         status = lib.flex_attn_fwd_aux(*args, max_scores.data_ptr(), *tail)
     _check(status)
     return out, lse, max_scores
+
+
+@dataclasses.dataclass
+class BlockMaskQ:
+    """The Q-side (transposed) lists of a BlockMask (int32 device tensors)."""
+    q_num_blocks: torch.Tensor
+    q_indices: torch.Tensor
+    full_q_num_blocks: torch.Tensor
+    full_q_indices: torch.Tensor
+    q_block: int
+    kv_block: int
+    L: int
+    S: int
+
+    def to_c(self) -> flex_block_mask_q:
+        cached = self.__dict__.get("_c")
+        if cached is not None:
+            return cached
+        c = flex_block_mask_q()
+        c.B, c.H = self.q_num_blocks.shape[0], self.q_num_blocks.shape[1]
+        c.q_block, c.kv_block = self.q_block, self.kv_block
+        c.num_kv_blocks, c.num_q_blocks = self.q_indices.shape[2], self.q_indices.shape[3]
+        c.q_num_blocks = self.q_num_blocks.data_ptr()
+        c.q_indices = self.q_indices.data_ptr()
+        c.full_q_num_blocks = self.full_q_num_blocks.data_ptr()
+        c.full_q_indices = self.full_q_indices.data_ptr()
+        self.__dict__["_c"] = c
+        return c
+
+
+def flex_blockmask_transpose(block_mask: BlockMask, out: Optional[BlockMaskQ] = None) -> BlockMaskQ:
+    """Fill the Q-side lists of a BlockMask on the GPU (C: flex_blockmask_transpose)."""
+    lib = load_library()
+    B, H, nqb, nkb = block_mask.kv_indices.shape
+    if out is None:
+        dev = block_mask.kv_indices.device
+        t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+        out = BlockMaskQ(t(B, H, nkb), t(B, H, nkb, nqb), t(B, H, nkb), t(B, H, nkb, nqb), block_mask.q_block,
+                         block_mask.kv_block, block_mask.L, block_mask.S)
+    cbm, cq = block_mask.to_c(), out.to_c()
+    _check(lib.flex_blockmask_transpose(ctypes.byref(cbm), ctypes.byref(cq),
+                                        ctypes.c_void_p(_stream_ptr(block_mask.kv_indices.device))))
+    return out
+
+
+def flex_attn_bwd_workspace_bytes(B: int, Hq: int, L: int) -> int:
+    return int(load_library().flex_attn_bwd_workspace_bytes(B, Hq, L))
+
+
+def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                  lse: torch.Tensor, *, block_mask: BlockMask, block_mask_q: BlockMaskQ,
+                  score: Optional[ScoreSpec] = None, mask: Optional[MaskSpec] = None, scale: Optional[float] = None,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients of sum(out * dout) with respect to q, k, v (C: flex_attn_bwd).
+
+    q, k, v, score, mask, scale and block_mask as for the flex_attn_fwd call
+    that returned out and lse; dout like out.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    score = score or ScoreSpec()
+    mask = mask or MaskSpec()
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if q.dim() != 4 or k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D or v.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or q.dtype not in DTYPES:
+        raise ValueError("q, k, v, out, dout must share a dtype, float32 or bfloat16")
+    for t in (q, k, v):
+        if t.stride(3) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    for t, shape in ((out, (B, Hq, L, D)), (dout, (B, Hq, L, D))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("out and dout must be contiguous (B, Hq, L, D)")
+    if tuple(lse.shape) != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 (B, Hq, L)")
+    if dq is None:
+        dq = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
+    ws_bytes = int(lib.flex_attn_bwd_workspace_bytes(B, Hq, L))
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    cs, cm = score.to_c(), mask.to_c(L, S)
+    cbm, cq = block_mask.to_c(), block_mask_q.to_c()
+    _check(lib.flex_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
+                             ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs),
+                             ctypes.byref(cm), ctypes.byref(cbm), ctypes.byref(cq), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), workspace.data_ptr(), ws_bytes,
+                             ctypes.c_void_p(_stream_ptr(q.device))))
+    return dq, dk, dv
 
 
 def default_scale(D: int) -> float:

@@ -1,0 +1,9 @@
+// Backward kernels instantiated for f32 inputs at head dimension 64 (one
+// translation unit per dtype and head dimension so they compile in parallel).
+#include "attn_bwd_impl.hpp"
+
+namespace flexmi {
+
+hipError_t launch_attn_bwd_f32_d64(const BwdArgs& a, hipStream_t stream) { return bwd_dispatch<float, 64>(a, stream); }
+
+}  // namespace flexmi

@@ -1,0 +1,740 @@
+// Block-sparse attention backward for gfx950 (CDNA4): dq, dk, dv.
+//
+// What is computed: the gradients of sum(out * dout) through the forward
+// definition (scaled score, score_mod g, -inf where mask_mod is false, row
+// softmax, weighted sum of values).  The charlestar blog "FlexAttention
+// score_mod / BlockMask" calls backward on the summed output of its example;
+// the 2kiu "PyTorch Flex Attention complete guide" (section 3.3) has the
+// backward walk Q-side lists obtained by transposing the KV-side lists, and
+// (sections 4.1 and 5.1) offers a deterministic dQ write order.  With
+// P = exp(z - lse) from the forward's lse and D_i = dout_i . out_i:
+//
+//   dS = P * (dout v^T - D) * g'(s) * scale,  g' = 1 - tanh(s/cap)^2 or 1
+//   dv = P^T dout,   dk = dS^T q,   dq = dS k
+//
+// How it maps onto CDNA4 (design of this library, not of the pages):
+//   * A row pass writes D_i and the base-2 lse per row (rows padded to a
+//     multiple of 128, +inf for rows that saw no key, so their P is 0).
+//   * Key-major pass (dk, dv): a workgroup owns 64 keys of one K/V head and
+//     walks their KV block's Q-side lists, for each query head of the GQA
+//     group in turn, so dk and dv of the K/V head are summed in registers.
+//     Wave (kh, qh) takes key half kh (32 keys) and query half qh of every
+//     64-query tile.  Scores are computed S = Q K^T, so each lane holds one key
+//     and 16 query rows: K and V rows stay in registers as the MFMA B operands
+//     of S and dP = dO V^T, the Q and dO tiles (with the rows' lse, D and
+//     document ids) stream through LDS, and P and dS feed dv^T += dO^T P and
+//     dk^T += Q^T dS straight from registers, the A operands coming from
+//     transposing LDS reads of the same tiles.  The two query halves are added
+//     once at the end.
+//   * Query-major pass (dq): the forward's layout.  A workgroup owns 64 query
+//     rows; wave (rg, kh) takes row group rg and key half kh of every K/V tile
+//     of the row block's KV-side lists.  S^T = K Q^T and dP^T = V dO^T with Q
+//     and dO rows in registers, so each lane holds one query row and its lse
+//     and D are per-lane scalars; dq^T += K^T dS^T.  The key halves are added
+//     once at the end.
+//   * Both passes recompute the scores, so nothing is accumulated with
+//     atomics: every output element is written once, by one workgroup, and
+//     the results do not depend on scheduling.
+//   * bf16 tiles arrive by LDS-DMA into a double buffer in the forward's
+//     swizzled layout; fp32 tiles are staged through registers into padded
+//     rows.
+#pragma once
+
+#include "attn_fwd_impl.hpp"
+
+namespace flexmi {
+
+namespace {
+
+// LDS geometry of one ring buffer of the backward passes: two row-major
+// 64-row tiles (Q and dO, or K and V), then the tile rows' base-2 lse and D
+// (key-major pass) and document ids.  bf16 rows are unpadded and swizzled as
+// in the forward (filled by LDS-DMA); fp32 rows are padded by four floats.
+template <typename T, int D> struct BwdTiles {
+    static constexpr int kStride = sizeof(T) == 2 ? D : D + Elem<float>::kPadK;   // elements per row
+    static constexpr int kTileBytes = kTileN * kStride * (int)sizeof(T);
+    static constexpr int kStatsOffset = 2 * kTileBytes;
+    static constexpr int kDocOffset = kStatsOffset + 2 * kTileN * 4;
+    static constexpr int kBufBytes = kDocOffset + kTileN * 4;
+    static_assert(kStride == Tiles<T, D>::kStrideK, "qk_block reads the first tile with this row stride");
+};
+
+// Waves per SIMD the backward kernels are compiled for.
+template <typename T, int D> struct BwdOccupancy {
+    static constexpr int kKeys = sizeof(T) == 2 ? 2 : 1;
+    static constexpr int kRows = sizeof(T) == 2 ? 2 : 1;
+};
+
+// Per-head constants of the score rule, base-2 units.
+struct BwdConsts {
+    float mul;      // NONE / ALIBI: scale*log2e; soft-cap kinds: 2*scale*log2e/cap
+    float c2;       // cap*log2e
+    float scale;
+    float alpha2;   // distance-bias slope * log2e of the query head (0 without bias)
+};
+
+__device__ __forceinline__ BwdConsts bwd_consts(const BwdArgs& a, int hq) {
+    BwdConsts c;
+    c.mul = a.mul;
+    c.c2 = a.c2;
+    c.scale = a.scale;
+    c.alpha2 = 0.0f;
+    if (a.score_kind == SCORE_SOFTCAP_ALIBI || a.score_kind == SCORE_ALIBI)
+        c.alpha2 = __builtin_amdgcn_exp2f(-(a.alibi_m * (float)(hq + 1)) / (float)a.Hq) * kLog2e;
+    return c;
+}
+
+// Base-2 score z2 = g(s) * log2e of accumulator acc (= q.k) plus the bias term
+// bias2 (base-2 distance bias, used by the ALiBi kinds), and gs = g'(s) * scale.
+// The soft-cap tanh is evaluated as 1 - 2 / (1 + e^{2y}), exact in the limits.
+template <int SCORE>
+__device__ __forceinline__ float score2(float acc, float bias2, const BwdConsts& c, float& gs) {
+    if constexpr (SCORE == SCORE_NONE) {
+        gs = c.scale;
+        return acc * c.mul;
+    } else if constexpr (SCORE == SCORE_ALIBI) {
+        gs = c.scale;
+        return __builtin_fmaf(acc, c.mul, bias2);
+    } else {
+        const float e = __builtin_amdgcn_exp2f(acc * c.mul);
+        const float r = __builtin_amdgcn_rcpf(1.0f + e);
+        const float t = __builtin_fmaf(-2.0f, r, 1.0f);
+        gs = __builtin_fmaf(-t * c.scale, t, c.scale);
+        if constexpr (SCORE == SCORE_SOFTCAP_ALIBI) return __builtin_fmaf(t, c.c2, bias2);
+        else return t * c.c2;
+    }
+}
+
+// Visibility in the key-major orientation: this lane's key `key` against the
+// query rows qr0 + acc_row(r, 0) (qr0 includes the lane half's row offset).
+// Sets z[r] = -inf where the mask hides the cell or the row is past L.
+// doc_rows holds the document ids of rows qr0 + 0..27 (LDS).
+template <bool EXT>
+__device__ __forceinline__ void apply_mask_keys(float (&z)[16], const MaskArgs& m, int key, int S, int L, int qr0,
+                                                int hq, int doc_k, const int* __restrict__ doc_rows) {
+    const int64_t p0 = (int64_t)qr0 + m.q_offset;            // position of row offset 0
+    uint32_t keep = key < S ? range_bits(0, (int64_t)L - qr0) : 0u;
+    const uint32_t causal = range_bits((int64_t)key - p0, 32);  // key <= p0 + o
+    auto doc_bits = [&]() -> uint32_t {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int4 d4 = *reinterpret_cast<const int4*>(doc_rows + 8 * g);
+            const int dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bits |= (dv[e] == doc_k) ? (1u << (8 * g + e)) : 0u;
+        }
+        return bits;
+    };
+    switch (m.kind) {
+    case MASK_NOOP: break;
+    case MASK_CAUSAL: keep &= causal; break;
+    case MASK_CAUSAL_WINDOW_SINKS: {
+        // p0 + o - key < window  <=>  o < key + window - p0
+        const uint32_t near = key < m.sinks ? ~0u : range_bits(0, (int64_t)key + m.window - p0);
+        keep &= causal & near;
+        break;
+    }
+    case MASK_PROGRAM: {
+        if constexpr (!EXT) break;   // program masks run in the extended kernels only
+        const uint32_t docb = m.uses_doc ? doc_bits() : 0u;
+#pragma unroll
+        for (int c = 0; c < kMaxClauses; ++c) {
+            if (c >= m.prog.n_clauses) break;
+            uint32_t any = 0;
+#pragma unroll
+            for (int l = 0; l < kMaxLiterals; ++l) {
+                if (l >= m.prog.n_lits[c]) break;
+                const int arg = m.prog.arg[c][l];
+                switch (m.prog.kind[c][l]) {
+                case PRED_CAUSAL: any |= causal; break;
+                case PRED_WINDOW: any |= range_bits(0, (int64_t)key + arg - p0); break;
+                case PRED_KV_LT: any |= key < arg ? ~0u : 0u; break;
+                case PRED_CHUNK: {                                      // p in key's chunk
+                    const int64_t lo = (int64_t)floor_div(key, arg) * arg;
+                    any |= range_bits(lo - p0, lo + arg - p0);
+                    break;
+                }
+                case PRED_STRIDE: {                                     // o = key - p0 (mod arg)
+                    int64_t rm = ((int64_t)key - p0) % arg;
+                    if (rm < 0) rm += arg;
+                    uint32_t bits = 0;
+                    if (arg >= 32) bits = rm < 32 ? 1u << (int)rm : 0u;
+                    else
+                        for (int o = (int)rm; o < 32; o += arg) bits |= 1u << o;
+                    any |= bits;
+                    break;
+                }
+                case PRED_DOC: any |= docb; break;
+                default: any |= hq < arg ? ~0u : 0u; break;             // h < arg
+                }
+            }
+            keep &= any;
+        }
+        break;
+    }
+    default: keep &= causal & doc_bits(); break;   // DOC_CAUSAL
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = (keep >> acc_row(r, 0)) & 1u ? z[r] : kNegInf;
+}
+
+// fp32: O^T += X^T P over rows [kb2*32, kb2*32 + 32) of a row-major padded
+// tile X (rows = the contracted index).  Lane (column c = lane & 31, half hf)
+// supplies P for row acc_row(r, hf) at step r, so the A operand is X[that
+// row][32*db + lane & 31]: consecutive lanes read consecutive floats.
+template <int D>
+__device__ __forceinline__ void xtp_f32(f32x16_t (&o)[D / 32], const float (&p)[16], const float* __restrict__ X,
+                                        int kb2, int lane) {
+    constexpr int kStride = BwdTiles<float, D>::kStride;
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const float* col = X + kb2 * 32 * kStride + db * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(col[acc_row(r, hf) * kStride], p[r], o[db], 0, 0, 0);
+    }
+}
+
+// O^T += X^T P for either dtype (X a row-major tile in LDS, 32-row block kb2).
+template <typename T, int D>
+__device__ __forceinline__ void xtp(f32x16_t (&o)[D / 32], const float (&p)[16], const char* __restrict__ X,
+                                    const LdsAddr<T, D>& la, int kb2, int lane) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x8_t pb[2];
+        pack_p(pb, p);
+        pv_bf16<D>(o, pb, X, la, kb2);
+    } else {
+        xtp_f32<D>(o, p, reinterpret_cast<const float*>(X), kb2, lane);
+    }
+}
+
+// fp32 staging of one tile's rows [row0, row0 + 64) of a slice with `rows`
+// valid rows (others read as zero) into a padded LDS tile.
+template <int D>
+__device__ __forceinline__ void fill_tile_f32(float* __restrict__ dst, const float* __restrict__ src, int64_t sr,
+                                              int row0, int rows, int tid) {
+    constexpr int kChunks = D / 4;
+    constexpr int kUnits = kTileN * kChunks / kThreads;
+    constexpr int kStride = BwdTiles<float, D>::kStride;
+    float4 v[kUnits];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const int c = tid + u * kThreads;
+        const int r = c / kChunks, ch = c % kChunks;
+        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (row0 + r < rows) v[u] = *reinterpret_cast<const float4*>(src + (int64_t)(row0 + r) * sr + ch * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+        const int c = tid + u * kThreads;
+        const int r = c / kChunks, ch = c % kChunks;
+        *reinterpret_cast<float4*>(dst + r * kStride + ch * 4) = v[u];
+    }
+}
+
+// Walks n tiles through a two-buffer LDS ring.  desc(t, masked) gives the
+// first row of tile t and whether its tile is partial; issue(buf, row0) starts
+// filling a buffer (bf16: LDS-DMA, asynchronous; fp32: through registers,
+// done on return); compute(buf, row0, masked) consumes a published buffer.
+// Per tile: wait for this wave's loads, barrier (publishes the tile and frees
+// the buffer computed last), refill that buffer with the next tile, compute.
+template <bool DMA, class Desc, class Issue, class Compute>
+__device__ __forceinline__ void walk_ring(int n, Desc&& desc, Issue&& issue, Compute&& compute, char* lds,
+                                          int buf_bytes) {
+    if (n <= 0) return;
+    int row[2] = {0, 0};
+    bool msk[2] = {false, false};
+    row[0] = desc(0, msk[0]);
+    issue(lds, row[0]);
+    auto step = [&](auto bc, int t) {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (DMA) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __builtin_amdgcn_s_barrier();
+        } else {
+            __syncthreads();
+        }
+        if (t + 1 < n) {
+            row[1 - B] = desc(t + 1, msk[1 - B]);
+            issue(lds + (1 - B) * buf_bytes, row[1 - B]);
+        }
+        compute(lds + B * buf_bytes, row[B], msk[B]);
+    };
+    for (int t = 0; t < n; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < n) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+    // every wave is done with the ring before the LDS is reused
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ row pass
+// lse2 = lse * log2(e) (+inf for rows with no visible key and padding rows)
+// and D_i = dout_i . out_i, for rows [0, Lp) of every (batch, query head).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_rows(BwdArgs a) {
+    constexpr int kChunk = 16 / (int)sizeof(T);
+    constexpr int kLanes = D / kChunk;                 // lanes per row
+    constexpr int kRowsPerBlock = kThreads / kLanes;
+    const int64_t n_rows = (int64_t)a.B * a.Hq * a.Lp;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
+    const int c = threadIdx.x % kLanes;
+    const bool in = row < n_rows;
+    const int64_t bh = in ? row / a.Lp : 0;
+    const int r = in ? (int)(row % a.Lp) : a.Lp;
+    float acc = 0.0f;
+    if (r < a.L) {
+        const int64_t off = (bh * a.L + r) * D + c * kChunk;
+        const uint4 o4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.out) + off);
+        const uint4 d4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.dout) + off);
+        if constexpr (sizeof(T) == 2) {
+            const bf16x8_t ov = __builtin_bit_cast(bf16x8_t, o4), dv = __builtin_bit_cast(bf16x8_t, d4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)ov[e], (float)dv[e], acc);
+        } else {
+            acc = __uint_as_float(o4.x) * __uint_as_float(d4.x);
+            acc = __builtin_fmaf(__uint_as_float(o4.y), __uint_as_float(d4.y), acc);
+            acc = __builtin_fmaf(__uint_as_float(o4.z), __uint_as_float(d4.z), acc);
+            acc = __builtin_fmaf(__uint_as_float(o4.w), __uint_as_float(d4.w), acc);
+        }
+    }
+#pragma unroll
+    for (int m = kLanes / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+    if (in && c == 0) {
+        float l2 = __builtin_inff();
+        if (r < a.L) {
+            const float lse = a.lse[bh * a.L + r];
+            if (lse > kNegInf) l2 = lse * kLog2e;
+        }
+        a.ws_lse2[row] = l2;
+        a.ws_dsum[row] = r < a.L ? acc : 0.0f;
+    }
+}
+
+// --------------------------------------------------------- key-major pass
+template <typename T, int D> struct DkdvLds {
+    static constexpr int kMergeBytes = 2 * 64 * D * 4;
+    static constexpr int value =
+        2 * BwdTiles<T, D>::kBufBytes > kMergeBytes ? 2 * BwdTiles<T, D>::kBufBytes : kMergeBytes;
+};
+
+template <typename T, int D, int SCORE, bool EXT>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
+    using G = BwdTiles<T, D>;
+    constexpr bool kDma = sizeof(T) == 2;
+
+    // Work item (K/V head slice bh, 64-key tile kt).  Workgroup i runs on XCD
+    // i % 8: when the items split evenly, each XCD takes whole K/V heads (their
+    // Q / dO tiles then stay in one L2) and walks them lowest key tile first
+    // (under causal-type masks it has the longest Q list).
+    const int subs = a.kv_block / kTileN;
+    const int per_bh = a.nKB * subs;
+    const int BH = a.B * a.Hkv;
+    const int items = BH * per_bh;
+    const int n = blockIdx.x;
+    int bh, kt;
+    if (items % 8 == 0 && (items / 8) % per_bh == 0) {
+        const int hpx = items / 8 / per_bh, k = n >> 3;
+        kt = k / hpx;
+        bh = (n & 7) * hpx + k % hpx;
+    } else {
+        kt = n / BH;
+        bh = n % BH;
+    }
+    const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+    const int kvb = kt / subs;
+    const int kv0 = kt * kTileN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), hf = lane >> 5;
+    const int kh = wave & 1, qh = wave >> 1;
+    const int key = kv0 + 32 * kh + (lane & 31);
+    const bool key_ok = key < a.S;
+    const bool with_doc = a.mask.uses_doc != 0;
+
+    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    QRegs<T, D> kr, vr;
+    load_q<T, D>(kr, kbase + (int64_t)key * a.k_sr, key_ok, hf);
+    load_q<T, D>(vr, vbase + (int64_t)key * a.v_sr, key_ok, hf);
+    const int doc_k = (with_doc && key_ok) ? __ldg(a.mask.doc_id + key) : -3;
+
+    f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        dk[db] = f32x16_t{};
+        dv[db] = f32x16_t{};
+    }
+    // bf16 LDS operand offsets with this wave's query half folded in
+    const LdsAddr<T, D> la = [&] {
+        if constexpr (sizeof(T) == 2) return lds_addr_bf16<D>(lane, qh);
+        else return LdsAddr<T, D>{};
+    }();
+    const int kb2 = sizeof(T) == 2 ? 0 : qh;
+    const int qsubs = a.q_block / kTileN;
+
+    for (int g = 0; g < a.group; ++g) {
+        const int hq = hkv * a.group + g;
+        const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
+        const int64_t col_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nKB + kvb;
+        const int n_part = min(max(scalar_load(a.q_num + col_id), 0), a.nQB);
+        const int n_full = min(max(scalar_load(a.fq_num + col_id), 0), a.nQB - n_part);
+        const int n_tiles = (n_part + n_full) * qsubs;
+        const int* part_idx = a.q_idx + col_id * a.nQB;
+        const int* full_idx = a.fq_idx + col_id * a.nQB;
+        const BwdConsts bc = bwd_consts(a, hq);
+
+        const T* qslice = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+        const T* dslice = reinterpret_cast<const T*>(a.dout) + ((int64_t)b * a.Hq + hq) * a.L * D;
+        const float* lslice = a.ws_lse2 + ((int64_t)b * a.Hq + hq) * a.Lp;
+        const float* sslice = a.ws_dsum + ((int64_t)b * a.Hq + hq) * a.Lp;
+
+        auto desc = [&](int t, bool& masked) -> int {
+            const int blk = qsubs == 1 ? t : t / qsubs;
+            const int sub = t - blk * qsubs;
+            int qb;
+            if (blk < n_part) {
+                qb = scalar_load(part_idx + blk);
+                masked = true;
+            } else {
+                qb = scalar_load(full_idx + (blk - n_part));
+                masked = false;
+            }
+            qb = min(max(qb, 0), a.nQB - 1);
+            return qb * a.q_block + sub * kTileN;
+        };
+
+        auto compute = [&](const char* cur, int q0, bool masked) {
+            const f32x16_t s = qk_block<T, D>(kr, cur, la, kb2, lane);
+            const f32x16_t dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
+            const float* st = reinterpret_cast<const float*>(cur + G::kStatsOffset) + 32 * qh + 4 * hf;
+            const int qr0 = q0 + 32 * qh + 4 * hf;
+            const float bias0 = bc.alpha2 * (float)(key - (qr0 + a.mask.q_offset));
+            float z[16], gs[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                z[r] = score2<SCORE>(s[r], __builtin_fmaf(-bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs[r]);
+            if (masked)
+                apply_mask_keys<EXT>(z, a.mask, key, a.S, a.L, qr0, hq, doc_k,
+                                     reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf);
+            float p[16], ds[16];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * gq);
+                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * gq);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dsv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * gq + e;
+                    p[r] = __builtin_amdgcn_exp2f(z[r] - lv[e]);
+                    ds[r] = p[r] * (dp[r] - dsv[e]) * gs[r];
+                }
+            }
+            xtp<T, D>(dv, p, cur + G::kTileBytes, la, kb2, lane);   // dv^T += dO^T P
+            xtp<T, D>(dk, ds, cur, la, kb2, lane);                  // dk^T += Q^T dS
+        };
+
+        if constexpr (kDma) {
+            const int q_row_bytes = (int)(a.q_sr * (int64_t)sizeof(T));
+            const int d_row_bytes = D * (int)sizeof(T);
+            const __amdgpu_buffer_rsrc_t rq = slice_rsrc(qslice, q_row_bytes, a.L);
+            const __amdgpu_buffer_rsrc_t rd = slice_rsrc(dslice, d_row_bytes, a.L);
+            const __amdgpu_buffer_rsrc_t rl = slice_rsrc(lslice, 4, a.Lp);
+            const __amdgpu_buffer_rsrc_t rs = slice_rsrc(sslice, 4, a.Lp);
+            const __amdgpu_buffer_rsrc_t rdoc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
+            const DmaPlan<D> pl = dma_plan<D>(q_row_bytes, d_row_bytes, wave, lane);
+            auto issue = [&](char* buf, int q0) {
+                const int qo = q0 * q_row_bytes, dof = q0 * d_row_bytes;
+#pragma unroll
+                for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16,
+                                                             pl.k[i], qo, 0, 0);
+#pragma unroll
+                for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rd, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024), 16, pl.v[i], dof, 0, 0);
+                const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
+                if (wave == 0)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_t*)(buf + G::kStatsOffset), 4, l4, q0 * 4,
+                                                             0, 0);
+                else if (wave == 1)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + G::kStatsOffset + 256), 4, l4,
+                                                             q0 * 4, 0, 0);
+                else if (wave == 2 && with_doc)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, l4,
+                                                             (q0 + a.mask.q_offset) * 4, 0, 0);
+            };
+            walk_ring<true>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
+        } else {
+            auto issue = [&](char* buf, int q0) {
+                fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(qslice), a.q_sr, q0,
+                                 a.L, tid);
+                fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(dslice),
+                                 D, q0, a.L, tid);
+                if (tid < 64) {
+                    reinterpret_cast<float*>(buf + G::kStatsOffset)[tid] = lslice[q0 + tid];
+                } else if (tid < 128) {
+                    reinterpret_cast<float*>(buf + G::kStatsOffset)[tid] = sslice[q0 + tid - 64];
+                } else if (tid < 192) {
+                    const int pos = q0 + (tid - 128) + a.mask.q_offset;
+                    int d = -1;
+                    if (with_doc && pos >= 0 && pos < a.mask.doc_len) d = a.mask.doc_id[pos];
+                    reinterpret_cast<int*>(buf + G::kDocOffset)[tid - 128] = d;
+                }
+            };
+            walk_ring<false>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
+        }
+    }
+
+    // Add the two query halves (qh = 1 hands its sums to qh = 0) and store.
+    float* slot = reinterpret_cast<float*>(lds) + (kh * 64 + lane) * D;
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                *reinterpret_cast<float4*>(slot + db * 16 + 4 * g) =
+                    make_float4(dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]);
+                *reinterpret_cast<float4*>(slot + D / 2 + db * 16 + 4 * g) =
+                    make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && key_ok) {
+        const int64_t orow = (((int64_t)b * a.Hkv + hkv) * a.S + key) * D;
+        T* dkrow = reinterpret_cast<T*>(a.dk) + orow;
+        T* dvrow = reinterpret_cast<T*>(a.dv) + orow;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 k4 = *reinterpret_cast<const float4*>(slot + db * 16 + 4 * g);
+                const float4 v4 = *reinterpret_cast<const float4*>(slot + D / 2 + db * 16 + 4 * g);
+                const int d0 = db * 32 + 8 * g + 4 * hf;
+                store_out4<T>(dkrow + d0, dk[db][4 * g] + k4.x, dk[db][4 * g + 1] + k4.y, dk[db][4 * g + 2] + k4.z,
+                              dk[db][4 * g + 3] + k4.w);
+                store_out4<T>(dvrow + d0, dv[db][4 * g] + v4.x, dv[db][4 * g + 1] + v4.y, dv[db][4 * g + 2] + v4.z,
+                              dv[db][4 * g + 3] + v4.w);
+            }
+    }
+}
+
+template <typename T, int D, int SCORE, bool EXT>
+__global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kKeys)) void attn_bwd_dkdv(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[DkdvLds<T, D>::value];
+    dkdv_body<T, D, SCORE, EXT>(a, lds);
+}
+
+// ------------------------------------------------------- query-major pass
+template <typename T, int D> struct DqLds {
+    static constexpr int kMergeBytes = 2 * 64 * (D / 2) * 4;
+    static constexpr int value =
+        2 * BwdTiles<T, D>::kBufBytes > kMergeBytes ? 2 * BwdTiles<T, D>::kBufBytes : kMergeBytes;
+};
+
+template <typename T, int D, int SCORE, bool EXT>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
+    using G = BwdTiles<T, D>;
+    constexpr bool kDma = sizeof(T) == 2;
+
+    // Highest Q block first (under causal-type masks it holds the most tiles);
+    // under GQA the query heads of one K/V head are kept on one XCD, as in the
+    // forward.
+    const int BH = a.B * a.Hq;
+    const int parts = a.q_block / 64;
+    const int qb = a.nQB - 1 - (int)(blockIdx.x / (BH * parts));
+    const int rem = (int)(blockIdx.x % (BH * parts));
+    const int part = rem / BH;
+    int bh = rem % BH;
+    if (a.group > 1 && BH % (8 * a.group) == 0) {
+        const int xcd = bh & 7, k = bh >> 3;
+        bh = (xcd + 8 * (k / a.group)) * a.group + k % a.group;
+    }
+    const int b = bh / a.Hq, hq = bh % a.Hq, hkv = hq / a.group;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), hf = lane >> 5;
+    const int rg = wave & 1, kh = wave >> 1;
+    const bool with_doc = a.mask.uses_doc != 0;
+
+    LaneRow row;
+    row.q_row = qb * a.q_block + part * 64 + rg * 32 + (lane & 31);
+    row.ok = row.q_row < a.L;
+    row.q_pos = row.q_row + a.mask.q_offset;
+    row.hq = hq;
+    row.doc_q = lane_doc(a.mask, row.q_pos);
+
+    const T* qbase = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+    const T* dslice = reinterpret_cast<const T*>(a.dout) + ((int64_t)b * a.Hq + hq) * a.L * D;
+    QRegs<T, D> qr, dor;
+    load_q<T, D>(qr, qbase + (int64_t)row.q_row * a.q_sr, row.ok, hf);
+    load_q<T, D>(dor, dslice + (int64_t)row.q_row * D, row.ok, hf);
+    const int64_t srow = ((int64_t)b * a.Hq + hq) * a.Lp + min(row.q_row, a.Lp - 1);
+    const float lse2 = row.ok ? a.ws_lse2[srow] : __builtin_inff();
+    const float dsum = row.ok ? a.ws_dsum[srow] : 0.0f;
+    const BwdConsts bc = bwd_consts(a, hq);
+
+    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+    const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
+    const int64_t row_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nQB + qb;
+    const int n_part = min(max(scalar_load(a.kv_num + row_id), 0), a.nKB);
+    const int n_full = min(max(scalar_load(a.full_num + row_id), 0), a.nKB - n_part);
+    const int ksubs = a.kv_block / kTileN;
+    const int n_tiles = (n_part + n_full) * ksubs;
+    const int* part_idx = a.kv_idx + row_id * a.nKB;
+    const int* full_idx = a.full_idx + row_id * a.nKB;
+
+    f32x16_t dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = f32x16_t{};
+    const LdsAddr<T, D> la = [&] {
+        if constexpr (sizeof(T) == 2) return lds_addr_bf16<D>(lane, kh);
+        else return LdsAddr<T, D>{};
+    }();
+    const int kb2 = sizeof(T) == 2 ? 0 : kh;
+
+    auto desc = [&](int t, bool& masked) -> int {
+        const int blk = ksubs == 1 ? t : t / ksubs;
+        const int sub = t - blk * ksubs;
+        int kb;
+        if (blk < n_part) {
+            kb = scalar_load(part_idx + blk);
+            masked = true;
+        } else {
+            kb = scalar_load(full_idx + (blk - n_part));
+            masked = false;
+        }
+        kb = min(max(kb, 0), a.nKB - 1);
+        return kb * a.kv_block + sub * kTileN;
+    };
+
+    auto compute = [&](const char* cur, int kv0, bool masked) {
+        const f32x16_t s = qk_block<T, D>(qr, cur, la, kb2, lane);
+        const f32x16_t dp = qk_block<T, D>(dor, cur + G::kTileBytes, la, kb2, lane);
+        const int key_base = kv0 + 32 * kh + 4 * hf;
+        const float bias0 = bc.alpha2 * (float)(key_base - row.q_pos);
+        float z[16], gs[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            z[r] = score2<SCORE>(s[r], __builtin_fmaf(bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs[r]);
+        if (masked) apply_mask<EXT>(z, a.mask, kv0, a.S, row, reinterpret_cast<const int*>(cur + G::kDocOffset), kh, hf);
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(z[r] - lse2);
+            ds[r] = p * (dp[r] - dsum) * gs[r];
+        }
+        xtp<T, D>(dq, ds, cur, la, kb2, lane);   // dq^T += K^T dS^T
+    };
+
+    if constexpr (kDma) {
+        const int k_row_bytes = (int)(a.k_sr * (int64_t)sizeof(T));
+        const int v_row_bytes = (int)(a.v_sr * (int64_t)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rk = slice_rsrc(kbase, k_row_bytes, a.S);
+        const __amdgpu_buffer_rsrc_t rv = slice_rsrc(vbase, v_row_bytes, a.S);
+        const __amdgpu_buffer_rsrc_t rdoc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
+        const DmaPlan<D> pl = dma_plan<D>(k_row_bytes, v_row_bytes, wave, lane);
+        auto issue = [&](char* buf, int kv0) {
+            const int ko = kv0 * k_row_bytes, vo = kv0 * v_row_bytes;
+#pragma unroll
+            for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
+                                                         ko, 0, 0);
+#pragma unroll
+            for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024),
+                                                         16, pl.v[i], vo, 0, 0);
+            if (with_doc && wave == 0) {
+                const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, l4, kv0 * 4, 0,
+                                                         0);
+            }
+        };
+        walk_ring<true>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
+    } else {
+        auto issue = [&](char* buf, int kv0) {
+            fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(kbase), a.k_sr, kv0, a.S,
+                             tid);
+            fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(vbase),
+                             a.v_sr, kv0, a.S, tid);
+            if (tid < 64) {
+                const int pos = kv0 + tid;
+                int d = -1;
+                if (with_doc && pos < a.mask.doc_len) d = a.mask.doc_id[pos];
+                reinterpret_cast<int*>(buf + G::kDocOffset)[tid] = d;
+            }
+        };
+        walk_ring<false>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
+    }
+
+    // Add the two key halves (kh = 1 hands its sums to kh = 0) and store.
+    float* slot = reinterpret_cast<float*>(lds) + (rg * 64 + lane) * (D / 2);
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<float4*>(slot + db * 16 + 4 * g) =
+                    make_float4(dq[db][4 * g], dq[db][4 * g + 1], dq[db][4 * g + 2], dq[db][4 * g + 3]);
+    }
+    __syncthreads();
+    if (kh == 0 && row.ok) {
+        T* dqrow = reinterpret_cast<T*>(a.dq) + (((int64_t)b * a.Hq + hq) * a.L + row.q_row) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 x = *reinterpret_cast<const float4*>(slot + db * 16 + 4 * g);
+                const int d0 = db * 32 + 8 * g + 4 * hf;
+                store_out4<T>(dqrow + d0, dq[db][4 * g] + x.x, dq[db][4 * g + 1] + x.y, dq[db][4 * g + 2] + x.z,
+                              dq[db][4 * g + 3] + x.w);
+            }
+    }
+}
+
+template <typename T, int D, int SCORE, bool EXT>
+__global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kRows)) void attn_bwd_dq(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D>::value];
+    dq_body<T, D, SCORE, EXT>(a, lds);
+}
+
+// ------------------------------------------------------------------ launch
+template <typename T, int D, int SCORE, bool EXT>
+hipError_t launch_bwd_passes(const BwdArgs& a, hipStream_t stream) {
+    const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKB * (a.kv_block / kTileN);
+    hipLaunchKernelGGL((attn_bwd_dkdv<T, D, SCORE, EXT>), dim3((unsigned)kv_items), dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t q_items = (int64_t)a.B * a.Hq * a.nQB * (a.q_block / 64);
+    hipLaunchKernelGGL((attn_bwd_dq<T, D, SCORE, EXT>), dim3((unsigned)q_items), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool EXT>
+hipError_t bwd_dispatch_score(const BwdArgs& a, hipStream_t stream) {
+    switch (a.score_kind) {
+    case SCORE_NONE: return launch_bwd_passes<T, D, SCORE_NONE, EXT>(a, stream);
+    case SCORE_SOFTCAP: return launch_bwd_passes<T, D, SCORE_SOFTCAP, EXT>(a, stream);
+    case SCORE_SOFTCAP_ALIBI: return launch_bwd_passes<T, D, SCORE_SOFTCAP_ALIBI, EXT>(a, stream);
+    case SCORE_ALIBI: return launch_bwd_passes<T, D, SCORE_ALIBI, EXT>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Row pass, then the key-major and query-major passes (program masks run in
+// separately compiled extended kernels, as in the forward).
+template <typename T, int D>
+hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t stream) {
+    constexpr int kRowsPerBlock = kThreads / (D / (16 / (int)sizeof(T)));
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Lp;
+    hipLaunchKernelGGL((attn_bwd_rows<T, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                       dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.mask.kind == MASK_PROGRAM) return bwd_dispatch_score<T, D, true>(a, stream);
+    return bwd_dispatch_score<T, D, false>(a, stream);
+}
+
+}  // namespace
+
+}  // namespace flexmi

@@ -348,4 +348,125 @@ flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32
     return FLEX_OK;
 }
 
+flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block_mask_q* bmq, void* stream) {
+    g_last_error.clear();
+    if (!bm || !bmq) return fail(FLEX_ERR_NULL, "bm and bmq must not be NULL");
+    if (flex_status s = check_bm_arrays(bm)) return s;
+    if (!bmq->q_num_blocks || !bmq->q_indices || !bmq->full_q_num_blocks || !bmq->full_q_indices)
+        return fail(FLEX_ERR_NULL, "Q-side block mask arrays must not be NULL");
+    if (bm->B < 1 || bm->H < 1 || bm->B > 65535 || bm->H > 65535 || bm->num_q_blocks < 1 || bm->num_kv_blocks < 1 ||
+        bm->q_block < 1 || bm->kv_block < 1)
+        return fail(FLEX_ERR_BLOCKMASK, "block mask dims out of range");
+    if (bmq->B != bm->B || bmq->H != bm->H || bmq->q_block != bm->q_block || bmq->kv_block != bm->kv_block ||
+        bmq->num_q_blocks != bm->num_q_blocks || bmq->num_kv_blocks != bm->num_kv_blocks)
+        return fail(FLEX_ERR_BLOCKMASK, "Q-side block mask dims differ from the block mask's");
+    if ((int64_t)bm->B * bm->H * bm->num_kv_blocks * bm->num_q_blocks >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_BLOCKMASK, "block mask lists above 2^31 entries are not supported");
+    TransposeArgs a;
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    a.q_num = bmq->q_num_blocks;
+    a.q_idx = bmq->q_indices;
+    a.fq_num = bmq->full_q_num_blocks;
+    a.fq_idx = bmq->full_q_indices;
+    a.Bm = bm->B;
+    a.Hm = bm->H;
+    a.nQB = bm->num_q_blocks;
+    a.nKB = bm->num_kv_blocks;
+    (void)hipGetLastError();
+    hipError_t e = launch_blockmask_transpose(a, as_stream(stream));
+    if (e != hipSuccess) return fail(FLEX_ERR_HIP, "block mask transpose launch failed: %s", hipGetErrorString(e));
+    return FLEX_OK;
+}
+
+size_t flex_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int64_t L) {
+    if (B < 1 || Hq < 1 || L < 1 || L >= kMaxLen) return 0;
+    return attn_bwd_workspace_bytes(B, Hq, (int)L);
+}
+
+flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
+                          int32_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                          const int64_t v_strides[3], float scale, const flex_score_params* score,
+                          const flex_mask_params* mask, const flex_block_mask* bm, const flex_block_mask_q* bmq,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
+                                  bm, out, lse))
+        return s;
+    if (!dout || !lse || !dq || !dk || !dv) return fail(FLEX_ERR_NULL, "dout, lse, dq, dk and dv must not be NULL");
+    if (!bmq) return fail(FLEX_ERR_NULL, "bmq must not be NULL");
+    if (!bmq->q_num_blocks || !bmq->q_indices || !bmq->full_q_num_blocks || !bmq->full_q_indices)
+        return fail(FLEX_ERR_NULL, "Q-side block mask arrays must not be NULL");
+    if (bmq->B != bm->B || bmq->H != bm->H || bmq->q_block != bm->q_block || bmq->kv_block != bm->kv_block ||
+        bmq->num_q_blocks != bm->num_q_blocks || bmq->num_kv_blocks != bm->num_kv_blocks)
+        return fail(FLEX_ERR_BLOCKMASK, "Q-side block mask dims differ from the block mask's");
+    if (bm->q_block != 64 && bm->q_block != 128)
+        return fail(FLEX_ERR_UNSUPPORTED, "the backward pass needs q_block 64 or 128 (got %d)", bm->q_block);
+    if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(FLEX_ERR_LAYOUT, "dout, dq, dk and dv must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FLEX_ERR_LAYOUT, "lse must be 4-byte aligned");
+    const int64_t elem = dtype == FLEX_BF16 ? 2 : 4;
+    if (L * std::max(q_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31) || L * D * elem >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_UNSUPPORTED, "one Q or dout head slice (L x row stride) must stay below 2 GiB");
+    if (q_strides[2] * elem * 128 >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_UNSUPPORTED, "Q row strides above 2^24 bytes are not supported");
+    const size_t need = attn_bwd_workspace_bytes(B, Hq, (int)L);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(FLEX_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(FLEX_ERR_LAYOUT, "workspace must be 16-byte aligned");
+
+    BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.Lp = (int)((L + 127) / 128 * 128);
+    a.ws_lse2 = reinterpret_cast<float*>(workspace);
+    a.ws_dsum = a.ws_lse2 + (size_t)B * Hq * a.Lp;
+    a.q_sb = q_strides[0]; a.q_sh = q_strides[1]; a.q_sr = q_strides[2];
+    a.k_sb = k_strides[0]; a.k_sh = k_strides[1]; a.k_sr = k_strides[2];
+    a.v_sb = v_strides[0]; a.v_sh = v_strides[1]; a.v_sr = v_strides[2];
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.L = (int)L;
+    a.S = (int)S;
+    a.group = Hq / Hkv;
+    a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+    a.score_kind = score->kind;
+    a.alibi_m = score->alibi_m;
+    const bool capped = score->kind == FLEX_SCORE_SOFTCAP || score->kind == FLEX_SCORE_SOFTCAP_ALIBI;
+    const double l2e = 1.4426950408889634;
+    a.mul = capped ? (float)(2.0 * (double)a.scale * l2e / (double)score->cap) : (float)((double)a.scale * l2e);
+    a.c2 = capped ? (float)((double)score->cap * l2e) : 0.0f;
+    a.mask = to_mask_args(mask);
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    a.q_num = bmq->q_num_blocks;
+    a.q_idx = bmq->q_indices;
+    a.fq_num = bmq->full_q_num_blocks;
+    a.fq_idx = bmq->full_q_indices;
+    a.Bm = bm->B;
+    a.Hm = bm->H;
+    a.nQB = bm->num_q_blocks;
+    a.nKB = bm->num_kv_blocks;
+    a.q_block = bm->q_block;
+    a.kv_block = bm->kv_block;
+    (void)hipGetLastError();
+    hipError_t e = launch_attn_bwd(dtype, D, a, as_stream(stream));
+    if (e != hipSuccess) return fail(FLEX_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return FLEX_OK;
+}
+
 }  // extern "C"

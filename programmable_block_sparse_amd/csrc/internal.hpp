@@ -23,6 +23,21 @@ struct BuildArgs {
 
 hipError_t launch_blockmask_build(const BuildArgs& a, hipStream_t stream);
 
+// Q-side lists of a block mask (the KV-side lists transposed).
+struct TransposeArgs {
+    const int* kv_num;
+    const int* kv_idx;
+    const int* full_num;
+    const int* full_idx;
+    int* q_num;
+    int* q_idx;
+    int* fq_num;
+    int* fq_idx;
+    int Bm, Hm, nQB, nKB;
+};
+
+hipError_t launch_blockmask_transpose(const TransposeArgs& a, hipStream_t stream);
+
 // Constants of the score rule that depend only on scale and cap (computed on
 // the host in double, rounded once).  Base-2 units: log2(e) is folded in.
 struct ScoreConsts {
@@ -95,5 +110,50 @@ hipError_t launch_attn_fwd(int dtype, int D, const FwdArgs& a, hipStream_t strea
 // Workspace bytes for the split-KV path; 0 when the prefill kernel is used.
 size_t attn_fwd_workspace_bytes(int dtype, int B, int Hq, int Hkv, int L, int S, int D,
                                 int q_block, int kv_block, int nKB, int Bm, int Hm);
+
+// Backward pass arguments.  q, k, v use element strides (last dim
+// contiguous); out, dout, dq are contiguous (B, Hq, L, D), dk, dv contiguous
+// (B, Hkv, S, D).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* ws_lse2;     // [B][Hq][Lp] lse * log2(e); +inf for rows with no key and padding rows
+    float* ws_dsum;     // [B][Hq][Lp] D_i = dout_i . out_i (0 for padding rows)
+    int Lp;             // L rounded up to a multiple of 64
+    int64_t q_sb, q_sh, q_sr;
+    int64_t k_sb, k_sh, k_sr;
+    int64_t v_sb, v_sh, v_sr;
+    int B, Hq, Hkv, L, S, group;
+    float scale;
+    int score_kind;
+    float alibi_m;
+    float mul;          // NONE / ALIBI: scale*log2e; soft-cap kinds: 2*scale*log2e/cap
+    float c2;           // cap*log2e
+    MaskArgs mask;
+    const int* kv_num;  // KV-side lists (the query-major pass)
+    const int* kv_idx;
+    const int* full_num;
+    const int* full_idx;
+    const int* q_num;   // Q-side lists (the key-major pass)
+    const int* q_idx;
+    const int* fq_num;
+    const int* fq_idx;
+    int Bm, Hm, nQB, nKB, q_block, kv_block;
+};
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int L);
+
+hipError_t launch_attn_bwd_bf16_d64(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_f32_d64(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_f32_d128(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd(int dtype, int D, const BwdArgs& a, hipStream_t stream);
 
 }  // namespace flexmi

@@ -248,3 +248,86 @@ def test_workspace_query_rejects_bad_shapes(lib):
     assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 3, 256, 256, 64, ctypes.byref(bm)) == 0
     assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 2, 256, 256, 96, ctypes.byref(bm)) == 0
     assert lib.flex_attn_fwd_workspace_bytes(1, 2, 4, 2, 256, 256, 64, None) == 0
+
+
+def _bmq(L, S, qb, kb, B=1, H=1):
+    c = pbs.flex_block_mask_q()
+    c.B, c.H, c.q_block, c.kv_block = B, H, qb, kb
+    c.num_q_blocks, c.num_kv_blocks = -(-L // qb), -(-S // kb)
+    c.q_num_blocks = c.q_indices = c.full_q_num_blocks = c.full_q_indices = FAKE
+    return c
+
+
+class Bwd(Fwd):
+    """Valid argument set for flex_attn_bwd; tests change one thing at a time."""
+
+    def __init__(self, **kw):
+        super().__init__(**kw)
+        self.dout = self.dq = self.dk = self.dv = FAKE
+        self.bmq = _bmq(self.L, self.S, self.bm.q_block, self.bm.kv_block)
+        self.ws = FAKE
+        self.ws_bytes = 2 * self.B * self.Hq * (-(-self.L // 128) * 128) * 4
+
+    def call(self, lib):
+        a3 = lambda x: None if x is None else (ctypes.c_int64 * 3)(*x)
+        ref = lambda x: None if x is None else ctypes.byref(x)
+        return lib.flex_attn_bwd(self.q, self.k, self.v, self.out, self.dout, self.lse, self.dtype, self.B, self.Hq,
+                                 self.Hkv, self.L, self.S, self.D, a3(self.qs), a3(self.ks), a3(self.vs),
+                                 ctypes.c_float(self.scale), ref(self.score), ref(self.mask), ref(self.bm),
+                                 ref(self.bmq), self.dq, self.dk, self.dv, self.ws, self.ws_bytes, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (lambda f: setattr(f, "dout", None), NULL),
+    (lambda f: setattr(f, "lse", None), NULL),
+    (lambda f: setattr(f, "dk", None), NULL),
+    (lambda f: setattr(f, "bmq", None), NULL),
+    (lambda f: setattr(f.bmq, "full_q_indices", None), NULL),
+    (lambda f: setattr(f, "Hkv", 3), GQA),
+    (lambda f: setattr(f.bmq, "num_kv_blocks", 3), BLOCKMASK),
+    (lambda f: setattr(f.bmq, "H", 4), BLOCKMASK),
+    (lambda f: (setattr(f.bm, "q_block", 32), setattr(f.bm, "num_q_blocks", 8),
+                setattr(f.bmq, "q_block", 32), setattr(f.bmq, "num_q_blocks", 8)), UNSUPPORTED),
+    (lambda f: setattr(f, "dq", FAKE + 8), LAYOUT),
+    (lambda f: setattr(f, "dv", FAKE + 2), LAYOUT),
+    (lambda f: setattr(f, "ws", None), WORKSPACE),
+    (lambda f: setattr(f, "ws_bytes", f.ws_bytes - 4), WORKSPACE),
+    (lambda f: setattr(f, "ws", FAKE + 4), LAYOUT),
+    (lambda f: setattr(f, "scale", float("nan")), PARAM),
+    (lambda f: setattr(f, "mask", _mask("causal_window_sinks", window=0)), PARAM),
+])
+def test_bwd_rejects(lib, change, code):
+    f = Bwd()
+    change(f)
+    assert f.call(lib) == code, pbs.flex_last_error()
+    assert pbs.flex_last_error() != ""
+
+
+def test_bwd_valid_call_reaches_the_launch(lib):
+    for kw in ({}, {"dtype": 0, "D": 128}, {"L": 100, "S": 300}):
+        f = Bwd(**kw)
+        assert f.call(lib) in (OK, HIP), pbs.flex_last_error()
+
+
+def test_bwd_workspace_bytes(lib):
+    # two float32 per (batch, query head, row), rows padded to a multiple of 128
+    assert lib.flex_attn_bwd_workspace_bytes(2, 3, 100) == 2 * 2 * 3 * 128 * 4
+    assert lib.flex_attn_bwd_workspace_bytes(1, 1, 129) == 2 * 256 * 4
+    assert lib.flex_attn_bwd_workspace_bytes(0, 1, 10) == 0
+    assert lib.flex_attn_bwd_workspace_bytes(1, 1, 0) == 0
+
+
+def test_transpose_rejects(lib):
+    bm, bmq = _bm(256, 300, 128, 64), _bmq(256, 300, 128, 64)
+    call = lambda a, b: lib.flex_blockmask_transpose(None if a is None else ctypes.byref(a),
+                                                     None if b is None else ctypes.byref(b), None)
+    assert call(bm, bmq) in (OK, HIP)
+    assert call(None, bmq) == NULL
+    assert call(bm, None) == NULL
+    bmq.q_indices = None
+    assert call(bm, bmq) == NULL
+    bmq = _bmq(256, 300, 128, 64)
+    bmq.num_q_blocks = 3
+    assert call(bm, bmq) == BLOCKMASK
+    bmq = _bmq(256, 300, 128, 64, B=2)
+    assert call(bm, bmq) == BLOCKMASK

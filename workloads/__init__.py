@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "draw_doc_lengths", "doc_ids_from_lengths",
     "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits", "make_inputs", "workload_doc_ids", "WORKLOAD_ORDER",
-    "EXTRA_WORKLOADS",
+    "EXTRA_WORKLOADS", "make_upstream",
 ]
 
 
@@ -165,3 +165,20 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, seed: Optional[int] = N
         else:
             out[name] = x
     return out
+
+
+def make_upstream(w: Workload, *, B: Optional[int] = None, seed: Optional[int] = None) -> dict:
+    """The gradient flowing into the attention output, for backward runs.
+
+    Standard normals of shape (B, Hq, L, D) from their own generator
+    (``PCG64(seed + 1_000_003)``) so the forward inputs stay as ``make_inputs``
+    draws them; bf16 workloads round them as in step 3 of the recipe.  Returns
+    ``dout`` (float32, exact widened values) and ``dout_bits`` for bf16.
+    """
+    rng = np.random.Generator(np.random.PCG64((w.seed if seed is None else seed) + 1_000_003))
+    B = w.B if B is None else B
+    x = rng.standard_normal((B, w.Hq, w.L, w.D), dtype=np.float32)
+    if w.dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return {"dout_bits": bits, "dout": bf16_bits_to_f32(bits)}
+    return {"dout": x}
