@@ -12,7 +12,15 @@ times the forward kernel alone with HIP events on the stream it runs on.  The
 CPU baseline times the float64 oracle on a bounded sample of the same workload
 and checks the GPU output on those rows.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --pass bwd a step is one training pass of the attention: BlockMask
+build, its Q-side transpose, the forward and the backward (dq, dk, dv).  Its
+throughput counts visited-block FLOPs of both directions: 4*D per cell forward
+and 10*D per cell backward (dV, dP, dK, dQ and the recomputed scores S: five
+products of 2*D each; the query-major pass recomputes S and dP, which is not
+counted).  The roofline entry then times the backward call (row pass,
+key-major and query-major passes) against its 10*D per cell.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
 """
 import argparse
 import json
@@ -37,6 +45,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="causal_softcap_alibi")
+    p.add_argument("--pass", dest="direction", choices=("fwd", "bwd"), default="fwd",
+                   help="fwd: the forward hot path (default); bwd: forward + backward training pass")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
@@ -125,6 +135,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.direction == "bwd":
+        main_bwd(args)
         return
 
     import torch
@@ -245,6 +258,175 @@ def main():
     if not args.no_cpu_baseline:
         result.update(cpu_baseline(args, w, inp, out, lse, flops))
     print(json.dumps(result), flush=True)
+
+
+def graph_runners(runners, dev, check):
+    """Capture each runner in its own HIP graph (on a side stream) and check
+    three replays of ``check``'s graph against the eager result, with eager work
+    between them.  Returns name -> replay."""
+    import torch
+    graphs = {}
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for name, fn in runners.items():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                fn()
+            graphs[name] = g
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    bufs, eager = check
+    ref = [b.clone() for b in bufs]
+    for i in range(3):
+        for b in bufs:
+            b.zero_()
+        graphs[next(iter(graphs))].replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(b, r) for b, r in zip(bufs, ref)):
+            raise RuntimeError(f"graph replay {i} differs from the eager result")
+        eager()
+        torch.cuda.synchronize()
+    return {name: g.replay for name, g in graphs.items()}
+
+
+def main_bwd(args):
+    import torch
+    import programmable_block_sparse_amd as pbs
+    from workloads import WORKLOADS, make_inputs, make_upstream
+    from workloads.torch_io import specs, to_device
+
+    w = WORKLOADS[args.workload]
+    if w.q_block not in (64, 128):
+        print(json.dumps({"error": f"the backward pass needs 64- or 128-row Q blocks ({w.name} has {w.q_block})"}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    up = make_upstream(w)
+    q, k, v, doc_t = to_device(w, inp, dev)
+    if w.dtype == "bf16":
+        dout = torch.from_numpy(up["dout_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        dout = torch.from_numpy(up["dout"]).to(dev)
+    mspec, sspec = specs(w, doc_t)
+    print(f"bench: backward, workload {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} L={w.L} S={w.S} D={w.D} {w.dtype} "
+          f"mask={w.mask} score={w.score} tiles {w.q_block}x{w.kv_block}", file=sys.stderr, flush=True)
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    bmq = pbs.flex_blockmask_transpose(bm)
+    torch.cuda.synchronize()
+    bm_np = {n: getattr(bm, n).cpu().numpy() for n in
+             ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices")}
+    fwd_flops = visited_flops_per_head(bm_np, w) * w.B * w.Hq        # 4*D per visited cell
+    bwd_flops = fwd_flops * 10 // 4                                    # 10*D per visited cell
+    out = torch.empty((w.B, w.Hq, w.L, w.D), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(out)
+    dk = torch.empty((w.B, w.Hkv, w.S, w.D), dtype=q.dtype, device=dev)
+    dv = torch.empty_like(dk)
+    ws_f = torch.empty(max(pbs.flex_attn_fwd_workspace_bytes(q.dtype, w.B, w.Hq, w.Hkv, w.L, w.S, w.D, bm), 1),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(pbs.flex_attn_bwd_workspace_bytes(q.dtype, w.B, w.Hq, w.Hkv, w.L, w.S, w.D, bm),
+                       dtype=torch.uint8, device=dev)
+    bm_step = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    bmq_step = pbs.flex_blockmask_transpose(bm_step)
+
+    def bwd():
+        pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=bm, block_mask_q=bmq, score=sspec, mask=mspec,
+                          dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    def step():
+        pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, out=bm_step)
+        pbs.flex_blockmask_transpose(bm_step, out=bmq_step)
+        pbs.flex_attn_fwd(q, k, v, block_mask=bm_step, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws_f)
+        pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=bm_step, block_mask_q=bmq_step, score=sspec,
+                          mask=mspec, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    def transpose_only():
+        pbs.flex_blockmask_transpose(bm_step, out=bmq_step)
+
+    def timed(fn, n):
+        stream = torch.cuda.current_stream(dev)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    runners = {"step": step, "bwd": bwd, "transpose": transpose_only}
+    mode = "eager"
+    if not args.eager:
+        runners = graph_runners(runners, dev, ([out, lse, dq, dk, dv], step))
+        mode = "hip_graph"
+    ms_step = timed(runners["step"], args.steps)
+    ms_bwd = timed(runners["bwd"], args.steps)
+    ms_tr = timed(runners["transpose"], args.steps)
+    print(f"bench: step {ms_step * 1e3:.1f} us, bwd {ms_bwd * 1e3:.1f} us, transpose {ms_tr * 1e3:.1f} us "
+          f"({mode})", file=sys.stderr, flush=True)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    bwd_tflops = bwd_flops / (ms_bwd * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": bwd_tflops, "peak": peak, "unit": "TFLOP/s", "frac": bwd_tflops / peak,
+            "traffic": None, "kernel": "attn_bwd_rows + attn_bwd_dkdv + attn_bwd_dq",
+            "algorithmic_per_launch": bwd_flops}
+    result = {
+        "metric": "flex fwd+bwd TFLOP/s (visited-block FLOPs: 4*D fwd + 10*D bwd per cell)",
+        "value": (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and upstream gradient, PCG64 seed %d)" % w.seed,
+        "config": {"workload": w.name + "_train", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S,
+                   "D": w.D, "mask": w.mask, "score": w.score, "cap": w.cap, "window": w.window,
+                   "sinks": w.sinks, "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset},
+        "roofline": roof, "bwd_ms": ms_bwd, "transpose_ms": ms_tr, "launch_mode": mode,
+        "bwd_tflops_visited": bwd_tflops, "fwd_visited_flops": fwd_flops, "bwd_visited_flops": bwd_flops,
+    }
+    if not args.no_cpu_baseline:
+        result.update(cpu_baseline_bwd(args, w, inp, up, (dq, dk, dv), bwd_flops))
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_bwd(args, w, inp, up, grads, flops):
+    """Time the float64 backward oracle on (batch, head) slices of the workload
+    (about 10 s) and compare the GPU gradients of those slices."""
+    from oracle import MaskMod, ScoreMod, attention_backward
+    import programmable_block_sparse_amd as pbs
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"], clauses=w.clauses)
+    smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
+    group = w.Hq // w.Hkv
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    sample, t_total, refs = [], 0.0, {}
+    for (b, h) in pairs:
+        t0 = time.perf_counter()
+        refs[(b, h)] = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=pbs.default_scale(w.D),
+                                          score=smod, mask=mmod, q_offset=w.q_offset, pairs=[(b, h)])
+        t_total += time.perf_counter() - t0
+        sample.append((b, h))
+        if (args.cpu_sample_heads and len(sample) >= args.cpu_sample_heads) or \
+                (not args.cpu_sample_heads and t_total >= 10.0):
+            break
+    dq = grads[0].float().cpu().numpy()
+    # dq of a sampled head is complete; dk, dv of a K/V head need all its query heads
+    err_dq = max(float(np.abs(dq[b, h] - refs[(b, h)][0][b, h]).max()) for (b, h) in sample)
+    return {
+        "cpu_baseline": {"value": flops / (w.B * w.Hq) * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
+                         "cores": blas_threads or cores, "kind": "oracle",
+                         "sample": f"{len(sample)} of {w.B * w.Hq} (batch, head) slices, all rows; float64 dense "
+                                   f"backward oracle, {t_total:.1f} s; host cores {cores}"},
+        "parity_on_bench_buffers": {"dq_max_abs": err_dq, "heads_checked": len(sample)},
+    }
 
 
 def cpu_baseline(args, w, inp, out, lse, flops):

@@ -288,10 +288,14 @@ typedef struct {
  * Errors: NULL, BLOCKMASK (dims differ or out of range), HIP. */
 flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block_mask_q* bmq, void* stream);
 
-/* Bytes of device workspace flex_attn_bwd needs: per (batch, query head, row,
- * rows padded to a multiple of 64) the base-2 lse and D_i = dO_i . O_i, as
- * float32.  Returns 0 for non-positive sizes. */
-size_t flex_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int64_t L);
+/* Bytes of device workspace flex_attn_bwd needs for these sizes: per (batch,
+ * query head, row, rows padded to a multiple of 128) the base-2 lse and
+ * D_i = dO_i . O_i as float32, plus, when one KV block's Q-side tiles may be
+ * shared by several workgroups (long columns: keys that every query sees),
+ * float32 partial sums of dk and dv for each share.  Returns 0 for arguments
+ * flex_attn_bwd would reject. */
+size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
+                                     int32_t D, const flex_block_mask* bm);
 
 /* Block-sparse attention backward: the gradients of sum(out * dout) with
  * respect to q, k and v for the forward of flex_attn_fwd (the charlestar blog
@@ -316,8 +320,9 @@ size_t flex_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int64_t L);
  *   dk, dv       device (B,Hkv,S,D) contiguous, dtype `dtype`
  *   workspace    device scratch of at least flex_attn_bwd_workspace_bytes(),
  *                16-byte aligned
- * Every output element is written exactly once (no atomics), so results do
- * not depend on scheduling.  bf16 outputs are rounded to nearest even from
+ * No output is accumulated with atomics: dq and, for most columns, dk and dv
+ * are written once by one workgroup; a long column's dk, dv partial sums are
+ * added in a fixed order.  Results do not depend on scheduling.  bf16 outputs are rounded to nearest even from
  * float32 accumulators.
  * Errors: NULL, SHAPE, GQA, BLOCKMASK, UNSUPPORTED, LAYOUT, WORKSPACE, PARAM,
  * HIP. */

@@ -11,7 +11,7 @@ the same names:
   flex_attn_fwd_workspace_bytes(...)
   flex_blockmask_transpose(block_mask) -> BlockMaskQ
   flex_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
-  flex_attn_bwd_workspace_bytes(B, Hq, L)
+  flex_attn_bwd_workspace_bytes(...)
   flex_status_string(code)
 
 There is no fallback: if the native library is missing or cannot load, every
@@ -112,7 +112,7 @@ def load_library():
     lib.flex_attn_fwd_aux.restype = ctypes.c_int
     lib.flex_blockmask_transpose.argtypes = [ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P]
     lib.flex_blockmask_transpose.restype = ctypes.c_int
-    lib.flex_attn_bwd_workspace_bytes.argtypes = [I32, I32, I64]
+    lib.flex_attn_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I64, I64, I32, ctypes.POINTER(flex_block_mask)]
     lib.flex_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3,
                                   ctypes.c_float, ctypes.POINTER(flex_score_params), ctypes.POINTER(flex_mask_params),
@@ -392,8 +392,10 @@ def flex_blockmask_transpose(block_mask: BlockMask, out: Optional[BlockMaskQ] = 
     return out
 
 
-def flex_attn_bwd_workspace_bytes(B: int, Hq: int, L: int) -> int:
-    return int(load_library().flex_attn_bwd_workspace_bytes(B, Hq, L))
+def flex_attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, Hq: int, Hkv: int, L: int, S: int, D: int,
+                                  block_mask: BlockMask) -> int:
+    cbm = block_mask.to_c()
+    return int(load_library().flex_attn_bwd_workspace_bytes(DTYPES[dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
 
 
 def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
@@ -428,12 +430,12 @@ def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
         dk = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
     if dv is None:
         dv = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
-    ws_bytes = int(lib.flex_attn_bwd_workspace_bytes(B, Hq, L))
+    cbm, cq = block_mask.to_c(), block_mask_q.to_c()
+    ws_bytes = int(lib.flex_attn_bwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     cs, cm = score.to_c(), mask.to_c(L, S)
-    cbm, cq = block_mask.to_c(), block_mask_q.to_c()
     _check(lib.flex_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                              lse.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
                              ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs),

@@ -46,6 +46,10 @@ namespace flexmi {
 
 namespace {
 
+// The LDS array seen in its own address space: DMA destinations are formed
+// there, so no generic-to-LDS conversion of a constant address is needed.
+typedef __attribute__((address_space(3))) char lds_char_t;
+
 // LDS geometry of one ring buffer of the backward passes: two row-major
 // 64-row tiles (Q and dO, or K and V), then the tile rows' base-2 lse and D
 // (key-major pass) and document ids.  bf16 rows are unpadded and swizzled as
@@ -58,6 +62,22 @@ template <typename T, int D> struct BwdTiles {
     static constexpr int kBufBytes = kDocOffset + kTileN * 4;
     static_assert(kStride == Tiles<T, D>::kStrideK, "qk_block reads the first tile with this row stride");
 };
+
+// LDS-DMA fill of a 64-row bf16 tile in the forward's swizzled layout (see
+// dma_plan): wave w's instruction i writes the 64 contiguous 16-byte chunks
+// (i*4 + w)*64 .. +63, lane l the one at position l.  The chunk a lane loads
+// depends on its row only modulo 16, and instruction i + 1 is 2048/D rows
+// further, so one per-lane byte offset serves every instruction; the row step
+// goes into the scalar offset.
+template <int D>
+__device__ __forceinline__ int dma_lane_offset(int row_bytes, int wave, int lane) {
+    constexpr int kChunksPerRow = D / 8;
+    const int pos = wave * 64 + lane;
+    const int row = pos / kChunksPerRow;
+    const int chunk = (pos % kChunksPerRow) ^ swz<D>(row);
+    return row * row_bytes + chunk * 16;
+}
+constexpr int dma_rows_per_inst(int D) { return 2048 / D; }
 
 // Waves per SIMD the backward kernels are compiled for.
 template <typename T, int D> struct BwdOccupancy {
@@ -105,17 +125,19 @@ __device__ __forceinline__ float score2(float acc, float bias2, const BwdConsts&
     }
 }
 
-// Visibility in the key-major orientation: this lane's key `key` against the
-// query rows qr0 + acc_row(r, 0) (qr0 includes the lane half's row offset).
-// Sets z[r] = -inf where the mask hides the cell or the row is past L.
-// doc_rows holds the document ids of rows qr0 + 0..27 (LDS).
+// Visibility in the key-major orientation: bit o of the result says whether
+// this lane's key `key` is visible from query row qr0 + o (qr0 includes the
+// lane half's row offset; the rows used are o = acc_row(r, 0)).  Rows past L
+// and keys past S are hidden.  doc_rows holds the document ids of rows
+// qr0 + 0..27 (LDS).
 template <bool EXT>
-__device__ __forceinline__ void apply_mask_keys(float (&z)[16], const MaskArgs& m, int key, int S, int L, int qr0,
-                                                int hq, int doc_k, const int* __restrict__ doc_rows) {
-    const int64_t p0 = (int64_t)qr0 + m.q_offset;            // position of row offset 0
+__device__ __forceinline__ uint32_t mask_bits_keys(const MaskArgs& m, int key, int S, int L, int qr0, int hq,
+                                                   int doc_k, const int* __restrict__ doc_rows) {
+    const int p0i = qr0 + m.q_offset;                        // position of row offset 0 (|p0| < 2^30)
+    const int64_t p0 = p0i;
     uint32_t keep = key < S ? range_bits(0, (int64_t)L - qr0) : 0u;
     const uint32_t causal = range_bits((int64_t)key - p0, 32);  // key <= p0 + o
-    auto doc_bits = [&]() -> uint32_t {
+    auto doc_bits = [&]() __attribute__((always_inline)) -> uint32_t {
         uint32_t bits = 0;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -156,12 +178,16 @@ __device__ __forceinline__ void apply_mask_keys(float (&z)[16], const MaskArgs& 
                     break;
                 }
                 case PRED_STRIDE: {                                     // o = key - p0 (mod arg)
-                    int64_t rm = ((int64_t)key - p0) % arg;
+                    // 32-bit residues (key >= 0, |p0| < 2^30): key - p0 itself
+                    // may not fit in 32 bits
+                    int p0m = p0i % arg;
+                    if (p0m < 0) p0m += arg;
+                    int rm = key % arg - p0m;
                     if (rm < 0) rm += arg;
                     uint32_t bits = 0;
-                    if (arg >= 32) bits = rm < 32 ? 1u << (int)rm : 0u;
+                    if (arg >= 32) bits = rm < 32 ? 1u << rm : 0u;
                     else
-                        for (int o = (int)rm; o < 32; o += arg) bits |= 1u << o;
+                        for (int o = rm; o < 32; o += arg) bits |= 1u << o;
                     any |= bits;
                     break;
                 }
@@ -175,8 +201,7 @@ __device__ __forceinline__ void apply_mask_keys(float (&z)[16], const MaskArgs& 
     }
     default: keep &= causal & doc_bits(); break;   // DOC_CAUSAL
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) z[r] = (keep >> acc_row(r, 0)) & 1u ? z[r] : kNegInf;
+    return keep;
 }
 
 // fp32: O^T += X^T P over rows [kb2*32, kb2*32 + 32) of a row-major padded
@@ -235,20 +260,21 @@ __device__ __forceinline__ void fill_tile_f32(float* __restrict__ dst, const flo
 }
 
 // Walks n tiles through a two-buffer LDS ring.  desc(t, masked) gives the
-// first row of tile t and whether its tile is partial; issue(buf, row0) starts
-// filling a buffer (bf16: LDS-DMA, asynchronous; fp32: through registers,
-// done on return); compute(buf, row0, masked) consumes a published buffer.
-// Per tile: wait for this wave's loads, barrier (publishes the tile and frees
-// the buffer computed last), refill that buffer with the next tile, compute.
+// first row of tile t and whether its tile is partial; issue(buffer, row0)
+// starts filling ring buffer 0 or 1 (bf16: LDS-DMA, asynchronous; fp32:
+// through registers, done on return); compute(buf, row0, masked) consumes a
+// published buffer.  Per tile: wait for this wave's loads, barrier (publishes
+// the tile and frees the buffer computed last), refill that buffer with the
+// next tile, compute.
 template <bool DMA, class Desc, class Issue, class Compute>
-__device__ __forceinline__ void walk_ring(int n, Desc&& desc, Issue&& issue, Compute&& compute, char* lds,
+__device__ __forceinline__ void walk_ring(int n, Desc&& desc, Issue&& issue, Compute&& compute, const char* lds,
                                           int buf_bytes) {
     if (n <= 0) return;
     int row[2] = {0, 0};
     bool msk[2] = {false, false};
     row[0] = desc(0, msk[0]);
-    issue(lds, row[0]);
-    auto step = [&](auto bc, int t) {
+    issue(std::integral_constant<int, 0>{}, row[0]);
+    auto step = [&](auto bc, int t) __attribute__((always_inline)) {
         constexpr int B = decltype(bc)::value;
         if constexpr (DMA) {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -258,7 +284,7 @@ __device__ __forceinline__ void walk_ring(int n, Desc&& desc, Issue&& issue, Com
         }
         if (t + 1 < n) {
             row[1 - B] = desc(t + 1, msk[1 - B]);
-            issue(lds + (1 - B) * buf_bytes, row[1 - B]);
+            issue(std::integral_constant<int, 1 - B>{}, row[1 - B]);
         }
         compute(lds + B * buf_bytes, row[B], msk[B]);
     };
@@ -314,6 +340,32 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_rows(BwdArgs a) {
 }
 
 // --------------------------------------------------------- key-major pass
+// Tiles of query head hq's Q-side list for KV block kvb (64-row tiles).
+__device__ __forceinline__ int bwd_head_tiles(const BwdArgs& a, int b, int hq, int kvb) {
+    const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
+    const int64_t col_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nKB + kvb;
+    const int n_part = min(max(scalar_load(a.q_num + col_id), 0), a.nQB);
+    const int n_full = min(max(scalar_load(a.fq_num + col_id), 0), a.nQB - n_part);
+    return (n_part + n_full) * (a.q_block / kTileN);
+}
+
+// Number of workgroups that share the key-major work of (batch b, K/V head
+// hkv, KV block kvb): its tile count over the group's query heads in units of
+// chunk_tiles, at most kv_splits.
+__device__ __forceinline__ int bwd_key_splits(const BwdArgs& a, int b, int hkv, int kvb) {
+    if (a.kv_splits <= 1) return 1;
+    int n = 0;
+    for (int g = 0; g < a.group; ++g) n += bwd_head_tiles(a, b, hkv * a.group + g, kvb);
+    return min(max((n + a.chunk_tiles - 1) / a.chunk_tiles, 1), a.kv_splits);
+}
+
+// fp32 partial sums of split `split` of 64-key column `col` (bh * per_bh + kt):
+// 64 x D for dk, then 64 x D for dv.
+__device__ __forceinline__ float* bwd_partial(const BwdArgs& a, int split, int col, int D) {
+    const int64_t cols = (int64_t)a.B * a.Hkv * a.nKB * (a.kv_block / kTileN);
+    return a.ws_part + ((int64_t)split * cols + col) * (2 * 64 * (int64_t)D);
+}
+
 template <typename T, int D> struct DkdvLds {
     static constexpr int kMergeBytes = 2 * 64 * D * 4;
     static constexpr int value =
@@ -321,19 +373,21 @@ template <typename T, int D> struct DkdvLds {
 };
 
 template <typename T, int D, int SCORE, bool EXT>
-__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_t* lds3) {
     using G = BwdTiles<T, D>;
     constexpr bool kDma = sizeof(T) == 2;
 
-    // Work item (K/V head slice bh, 64-key tile kt).  Workgroup i runs on XCD
-    // i % 8: when the items split evenly, each XCD takes whole K/V heads (their
-    // Q / dO tiles then stay in one L2) and walks them lowest key tile first
-    // (under causal-type masks it has the longest Q list).
+    // Work item (K/V head slice bh, 64-key tile kt) and split of its Q-side
+    // tile sequence.  Workgroup i runs on XCD i % 8: when the items split
+    // evenly, each XCD takes whole K/V heads (their Q / dO tiles then stay in
+    // one L2) and walks them lowest key tile first (under causal-type masks it
+    // has the longest Q list).
     const int subs = a.kv_block / kTileN;
     const int per_bh = a.nKB * subs;
     const int BH = a.B * a.Hkv;
     const int items = BH * per_bh;
-    const int n = blockIdx.x;
+    const int split = (int)(blockIdx.x / items);
+    const int n = (int)(blockIdx.x % items);
     int bh, kt;
     if (items % 8 == 0 && (items / 8) % per_bh == 0) {
         const int hpx = items / 8 / per_bh, k = n >> 3;
@@ -373,13 +427,28 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
     const int kb2 = sizeof(T) == 2 ? 0 : qh;
     const int qsubs = a.q_block / kTileN;
 
+    // The column's tiles over all query heads of the group, as one sequence;
+    // a long one is cut into up to kv_splits contiguous ranges of about
+    // chunk_tiles tiles, one per workgroup (their partial sums are added in
+    // split order by attn_bwd_dkdv_reduce).
+    const int nch = bwd_key_splits(a, b, hkv, kvb);
+    if (split >= nch) return;
+    int n_col = 0;
+    for (int g = 0; g < a.group; ++g) n_col += bwd_head_tiles(a, b, hkv * a.group + g, kvb);
+    const int t_lo = (int)((int64_t)n_col * split / nch), t_hi = (int)((int64_t)n_col * (split + 1) / nch);
+
+    int base = 0;
     for (int g = 0; g < a.group; ++g) {
         const int hq = hkv * a.group + g;
         const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
         const int64_t col_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nKB + kvb;
         const int n_part = min(max(scalar_load(a.q_num + col_id), 0), a.nQB);
         const int n_full = min(max(scalar_load(a.fq_num + col_id), 0), a.nQB - n_part);
-        const int n_tiles = (n_part + n_full) * qsubs;
+        const int head_tiles = (n_part + n_full) * qsubs;
+        const int lo = max(t_lo - base, 0), hi = min(t_hi - base, head_tiles);
+        base += head_tiles;
+        if (lo >= hi) continue;
+        const int n_tiles = hi - lo;
         const int* part_idx = a.q_idx + col_id * a.nQB;
         const int* full_idx = a.fq_idx + col_id * a.nQB;
         const BwdConsts bc = bwd_consts(a, hq);
@@ -389,7 +458,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
         const float* lslice = a.ws_lse2 + ((int64_t)b * a.Hq + hq) * a.Lp;
         const float* sslice = a.ws_dsum + ((int64_t)b * a.Hq + hq) * a.Lp;
 
-        auto desc = [&](int t, bool& masked) -> int {
+        auto desc = [&](int t, bool& masked) __attribute__((always_inline)) -> int {
+            t += lo;
             const int blk = qsubs == 1 ? t : t / qsubs;
             const int sub = t - blk * qsubs;
             int qb;
@@ -404,34 +474,48 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
             return qb * a.q_block + sub * kTileN;
         };
 
-        auto compute = [&](const char* cur, int q0, bool masked) {
-            const f32x16_t s = qk_block<T, D>(kr, cur, la, kb2, lane);
-            const f32x16_t dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
-            const float* st = reinterpret_cast<const float*>(cur + G::kStatsOffset) + 32 * qh + 4 * hf;
+        auto compute = [&](const char* cur, int q0, bool masked) __attribute__((always_inline)) {
             const int qr0 = q0 + 32 * qh + 4 * hf;
+            const uint32_t keep =
+                masked ? mask_bits_keys<EXT>(a.mask, key, a.S, a.L, qr0, hq, doc_k,
+                                             reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf)
+                       : ~0u;
+            const float* st = reinterpret_cast<const float*>(cur + G::kStatsOffset) + 32 * qh + 4 * hf;
             const float bias0 = bc.alpha2 * (float)(key - (qr0 + a.mask.q_offset));
-            float z[16], gs[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                z[r] = score2<SCORE>(s[r], __builtin_fmaf(-bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs[r]);
-            if (masked)
-                apply_mask_keys<EXT>(z, a.mask, key, a.S, a.L, qr0, hq, doc_k,
-                                     reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf);
-            float p[16], ds[16];
+            // head dim 64: both score-shaped products first (independent MFMA
+            // work to overlap with the exponentials); head dim 128: dP after
+            // the dV product, so fewer registers are live at once
+            const f32x16_t s = qk_block<T, D>(kr, cur, la, kb2, lane);
+            f32x16_t dp;
+            if constexpr (D == 64) dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
+            float p[16], pg[16];   // P, and P * g'(s) * scale
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * gq);
-                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * gq);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dsv[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * gq + e;
-                    p[r] = __builtin_amdgcn_exp2f(z[r] - lv[e]);
-                    ds[r] = p[r] * (dp[r] - dsv[e]) * gs[r];
+                    float gs;
+                    float z = score2<SCORE>(s[r], __builtin_fmaf(-bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs);
+                    z = (keep >> acc_row(r, 0)) & 1u ? z : kNegInf;
+                    p[r] = __builtin_amdgcn_exp2f(z - lv[e]);
+                    pg[r] = p[r] * gs;
                 }
             }
             xtp<T, D>(dv, p, cur + G::kTileBytes, la, kb2, lane);   // dv^T += dO^T P
-            xtp<T, D>(dk, ds, cur, la, kb2, lane);                  // dk^T += Q^T dS
+            if constexpr (D != 64) dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * gq);
+                const float dsv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * gq + e;
+                    pg[r] *= dp[r] - dsv[e];                              // dS
+                }
+            }
+            xtp<T, D>(dk, pg, cur, la, kb2, lane);                 // dk^T += Q^T dS
         };
 
         if constexpr (kDma) {
@@ -442,17 +526,19 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
             const __amdgpu_buffer_rsrc_t rl = slice_rsrc(lslice, 4, a.Lp);
             const __amdgpu_buffer_rsrc_t rs = slice_rsrc(sslice, 4, a.Lp);
             const __amdgpu_buffer_rsrc_t rdoc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
-            const DmaPlan<D> pl = dma_plan<D>(q_row_bytes, d_row_bytes, wave, lane);
-            auto issue = [&](char* buf, int q0) {
-                const int qo = q0 * q_row_bytes, dof = q0 * d_row_bytes;
+            const int oq = dma_lane_offset<D>(q_row_bytes, wave, lane);
+            const int od = dma_lane_offset<D>(d_row_bytes, wave, lane);
+            auto issue = [&](auto bi, int q0) __attribute__((always_inline)) {
+                lds_char_t* buf = lds3 + decltype(bi)::value * G::kBufBytes;
 #pragma unroll
-                for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16,
-                                                             pl.k[i], qo, 0, 0);
+                for (int i = 0; i < D / 32; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, oq,
+                                                             (q0 + i * dma_rows_per_inst(D)) * q_row_bytes, 0, 0);
 #pragma unroll
-                for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+                for (int i = 0; i < D / 32; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rd, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024), 16, pl.v[i], dof, 0, 0);
+                        rd, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024), 16, od,
+                        (q0 + i * dma_rows_per_inst(D)) * d_row_bytes, 0, 0);
                 const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
                 if (wave == 0)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_t*)(buf + G::kStatsOffset), 4, l4, q0 * 4,
@@ -466,7 +552,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
             };
             walk_ring<true>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
         } else {
-            auto issue = [&](char* buf, int q0) {
+            auto issue = [&](auto bi, int q0) __attribute__((always_inline)) {
+                char* buf = lds + decltype(bi)::value * G::kBufBytes;
                 fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(qslice), a.q_sr, q0,
                                  a.L, tid);
                 fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(dslice),
@@ -501,28 +588,76 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds) {
     }
     __syncthreads();
     if (qh == 0 && key_ok) {
-        const int64_t orow = (((int64_t)b * a.Hkv + hkv) * a.S + key) * D;
-        T* dkrow = reinterpret_cast<T*>(a.dk) + orow;
-        T* dvrow = reinterpret_cast<T*>(a.dv) + orow;
+        if (nch == 1) {
+            const int64_t orow = (((int64_t)b * a.Hkv + hkv) * a.S + key) * D;
+            T* dkrow = reinterpret_cast<T*>(a.dk) + orow;
+            T* dvrow = reinterpret_cast<T*>(a.dv) + orow;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 k4 = *reinterpret_cast<const float4*>(slot + db * 16 + 4 * g);
-                const float4 v4 = *reinterpret_cast<const float4*>(slot + D / 2 + db * 16 + 4 * g);
-                const int d0 = db * 32 + 8 * g + 4 * hf;
-                store_out4<T>(dkrow + d0, dk[db][4 * g] + k4.x, dk[db][4 * g + 1] + k4.y, dk[db][4 * g + 2] + k4.z,
-                              dk[db][4 * g + 3] + k4.w);
-                store_out4<T>(dvrow + d0, dv[db][4 * g] + v4.x, dv[db][4 * g + 1] + v4.y, dv[db][4 * g + 2] + v4.z,
-                              dv[db][4 * g + 3] + v4.w);
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(slot + db * 16 + 4 * g);
+                    const float4 v4 = *reinterpret_cast<const float4*>(slot + D / 2 + db * 16 + 4 * g);
+                    const int d0 = db * 32 + 8 * g + 4 * hf;
+                    store_out4<T>(dkrow + d0, dk[db][4 * g] + k4.x, dk[db][4 * g + 1] + k4.y,
+                                  dk[db][4 * g + 2] + k4.z, dk[db][4 * g + 3] + k4.w);
+                    store_out4<T>(dvrow + d0, dv[db][4 * g] + v4.x, dv[db][4 * g + 1] + v4.y,
+                                  dv[db][4 * g + 2] + v4.z, dv[db][4 * g + 3] + v4.w);
+                }
+        } else {
+            // fp32 partial sums of this split: [key][D] for dk, then for dv
+            float* part = bwd_partial(a, split, bh * per_bh + kt, D) + (key - kv0) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(slot + db * 16 + 4 * g);
+                    const float4 v4 = *reinterpret_cast<const float4*>(slot + D / 2 + db * 16 + 4 * g);
+                    const int d0 = db * 32 + 8 * g + 4 * hf;
+                    *reinterpret_cast<float4*>(part + d0) =
+                        make_float4(dk[db][4 * g] + k4.x, dk[db][4 * g + 1] + k4.y, dk[db][4 * g + 2] + k4.z,
+                                    dk[db][4 * g + 3] + k4.w);
+                    *reinterpret_cast<float4*>(part + 64 * D + d0) =
+                        make_float4(dv[db][4 * g] + v4.x, dv[db][4 * g + 1] + v4.y, dv[db][4 * g + 2] + v4.z,
+                                    dv[db][4 * g + 3] + v4.w);
+                }
+        }
     }
 }
 
 template <typename T, int D, int SCORE, bool EXT>
 __global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kKeys)) void attn_bwd_dkdv(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[DkdvLds<T, D>::value];
-    dkdv_body<T, D, SCORE, EXT>(a, lds);
+    dkdv_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds);
+}
+
+// Adds the split partial sums of the columns the key-major pass cut, in
+// split order, and writes dk, dv (one workgroup per 64-key column).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_reduce(BwdArgs a) {
+    const int subs = a.kv_block / kTileN;
+    const int per_bh = a.nKB * subs;
+    const int col = blockIdx.x;
+    const int bh = col / per_bh, kt = col % per_bh;
+    const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+    const int nch = bwd_key_splits(a, b, hkv, kt / subs);
+    if (nch == 1) return;
+    const int kv0 = kt * kTileN;
+    for (int e = threadIdx.x * 4; e < 64 * D; e += kThreads * 4) {
+        const int key = kv0 + e / D, d = e % D;
+        if (key >= a.S) break;
+        float4 sk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sv = sk;
+        for (int sp = 0; sp < nch; ++sp) {
+            const float* part = bwd_partial(a, sp, col, D);
+            const float4 k4 = *reinterpret_cast<const float4*>(part + e);
+            const float4 v4 = *reinterpret_cast<const float4*>(part + 64 * D + e);
+            sk.x += k4.x; sk.y += k4.y; sk.z += k4.z; sk.w += k4.w;
+            sv.x += v4.x; sv.y += v4.y; sv.z += v4.z; sv.w += v4.w;
+        }
+        const int64_t o = ((int64_t)bh * a.S + key) * D + d;
+        store_out4<T>(reinterpret_cast<T*>(a.dk) + o, sk.x, sk.y, sk.z, sk.w);
+        store_out4<T>(reinterpret_cast<T*>(a.dv) + o, sv.x, sv.y, sv.z, sv.w);
+    }
 }
 
 // ------------------------------------------------------- query-major pass
@@ -533,7 +668,7 @@ template <typename T, int D> struct DqLds {
 };
 
 template <typename T, int D, int SCORE, bool EXT>
-__device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t* lds3) {
     using G = BwdTiles<T, D>;
     constexpr bool kDma = sizeof(T) == 2;
 
@@ -593,7 +728,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
     }();
     const int kb2 = sizeof(T) == 2 ? 0 : kh;
 
-    auto desc = [&](int t, bool& masked) -> int {
+    auto desc = [&](int t, bool& masked) __attribute__((always_inline)) -> int {
         const int blk = ksubs == 1 ? t : t / ksubs;
         const int sub = t - blk * ksubs;
         int kb;
@@ -608,7 +743,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
         return kb * a.kv_block + sub * kTileN;
     };
 
-    auto compute = [&](const char* cur, int kv0, bool masked) {
+    auto compute = [&](const char* cur, int kv0, bool masked) __attribute__((always_inline)) {
         const f32x16_t s = qk_block<T, D>(qr, cur, la, kb2, lane);
         const f32x16_t dp = qk_block<T, D>(dor, cur + G::kTileBytes, la, kb2, lane);
         const int key_base = kv0 + 32 * kh + 4 * hf;
@@ -633,17 +768,18 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
         const __amdgpu_buffer_rsrc_t rk = slice_rsrc(kbase, k_row_bytes, a.S);
         const __amdgpu_buffer_rsrc_t rv = slice_rsrc(vbase, v_row_bytes, a.S);
         const __amdgpu_buffer_rsrc_t rdoc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
-        const DmaPlan<D> pl = dma_plan<D>(k_row_bytes, v_row_bytes, wave, lane);
-        auto issue = [&](char* buf, int kv0) {
-            const int ko = kv0 * k_row_bytes, vo = kv0 * v_row_bytes;
+        const int ok_ = dma_lane_offset<D>(k_row_bytes, wave, lane);
+        const int ov = dma_lane_offset<D>(v_row_bytes, wave, lane);
+        auto issue = [&](auto bi, int kv0) __attribute__((always_inline)) {
+            lds_char_t* buf = lds3 + decltype(bi)::value * G::kBufBytes;
 #pragma unroll
-            for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
-                                                         ko, 0, 0);
+            for (int i = 0; i < D / 32; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, ok_,
+                                                         (kv0 + i * dma_rows_per_inst(D)) * k_row_bytes, 0, 0);
 #pragma unroll
-            for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
+            for (int i = 0; i < D / 32; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024),
-                                                         16, pl.v[i], vo, 0, 0);
+                                                         16, ov, (kv0 + i * dma_rows_per_inst(D)) * v_row_bytes, 0, 0);
             if (with_doc && wave == 0) {
                 const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, l4, kv0 * 4, 0,
@@ -652,7 +788,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
         };
         walk_ring<true>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
     } else {
-        auto issue = [&](char* buf, int kv0) {
+        auto issue = [&](auto bi, int kv0) __attribute__((always_inline)) {
+            char* buf = lds + decltype(bi)::value * G::kBufBytes;
             fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(kbase), a.k_sr, kv0, a.S,
                              tid);
             fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(vbase),
@@ -695,16 +832,22 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds) {
 template <typename T, int D, int SCORE, bool EXT>
 __global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kRows)) void attn_bwd_dq(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D>::value];
-    dq_body<T, D, SCORE, EXT>(a, lds);
+    dq_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds);
 }
 
 // ------------------------------------------------------------------ launch
 template <typename T, int D, int SCORE, bool EXT>
 hipError_t launch_bwd_passes(const BwdArgs& a, hipStream_t stream) {
     const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKB * (a.kv_block / kTileN);
-    hipLaunchKernelGGL((attn_bwd_dkdv<T, D, SCORE, EXT>), dim3((unsigned)kv_items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv<T, D, SCORE, EXT>), dim3((unsigned)(kv_items * a.kv_splits)), dim3(kThreads), 0,
+                       stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.kv_splits > 1) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_reduce<T, D>), dim3((unsigned)kv_items), dim3(kThreads), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t q_items = (int64_t)a.B * a.Hq * a.nQB * (a.q_block / 64);
     hipLaunchKernelGGL((attn_bwd_dq<T, D, SCORE, EXT>), dim3((unsigned)q_items), dim3(kThreads), 0, stream, a);
     return hipGetLastError();

@@ -381,9 +381,13 @@ flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block
     return FLEX_OK;
 }
 
-size_t flex_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int64_t L) {
-    if (B < 1 || Hq < 1 || L < 1 || L >= kMaxLen) return 0;
-    return attn_bwd_workspace_bytes(B, Hq, (int)L);
+size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
+                                     int32_t D, const flex_block_mask* bm) {
+    if (!bm || B < 1 || Hq < 1 || Hkv < 1 || L < 1 || S < 1 || L >= kMaxLen || S >= kMaxLen || Hq % Hkv) return 0;
+    if ((dtype != FLEX_F32 && dtype != FLEX_BF16) || (D != 64 && D != 128)) return 0;
+    if ((bm->q_block != 64 && bm->q_block != 128) || bm->kv_block < 64 || bm->kv_block % 64) return 0;
+    return attn_bwd_workspace_bytes(B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block, bm->num_q_blocks,
+                                    bm->num_kv_blocks);
 }
 
 flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -414,7 +418,8 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
         return fail(FLEX_ERR_UNSUPPORTED, "one Q or dout head slice (L x row stride) must stay below 2 GiB");
     if (q_strides[2] * elem * 128 >= (int64_t(1) << 31))
         return fail(FLEX_ERR_UNSUPPORTED, "Q row strides above 2^24 bytes are not supported");
-    const size_t need = attn_bwd_workspace_bytes(B, Hq, (int)L);
+    const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block,
+                                                 bm->num_q_blocks, bm->num_kv_blocks);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FLEX_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(FLEX_ERR_LAYOUT, "workspace must be 16-byte aligned");
@@ -432,6 +437,9 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
     a.Lp = (int)((L + 127) / 128 * 128);
     a.ws_lse2 = reinterpret_cast<float*>(workspace);
     a.ws_dsum = a.ws_lse2 + (size_t)B * Hq * a.Lp;
+    a.kv_splits = bwd_kv_splits(Hq / Hkv, bm->num_q_blocks, bm->q_block);
+    a.chunk_tiles = kBwdChunkTiles;
+    a.ws_part = a.kv_splits > 1 ? a.ws_dsum + (size_t)B * Hq * a.Lp : nullptr;
     a.q_sb = q_strides[0]; a.q_sh = q_strides[1]; a.q_sr = q_strides[2];
     a.k_sb = k_strides[0]; a.k_sh = k_strides[1]; a.k_sr = k_strides[2];
     a.v_sb = v_strides[0]; a.v_sh = v_strides[1]; a.v_sr = v_strides[2];

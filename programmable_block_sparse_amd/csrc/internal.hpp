@@ -126,7 +126,10 @@ struct BwdArgs {
     void* dv;
     float* ws_lse2;     // [B][Hq][Lp] lse * log2(e); +inf for rows with no key and padding rows
     float* ws_dsum;     // [B][Hq][Lp] D_i = dout_i . out_i (0 for padding rows)
-    int Lp;             // L rounded up to a multiple of 64
+    float* ws_part;     // [kv_splits][B*Hkv*S/64 columns][2][64][D] fp32 partial dk, dv (kv_splits > 1)
+    int Lp;             // L rounded up to a multiple of 128
+    int kv_splits;      // most workgroups sharing one 64-key column of the key-major pass
+    int chunk_tiles;    // Q-side tiles per share
     int64_t q_sb, q_sh, q_sr;
     int64_t k_sb, k_sh, k_sr;
     int64_t v_sb, v_sh, v_sr;
@@ -148,7 +151,15 @@ struct BwdArgs {
     int Bm, Hm, nQB, nKB, q_block, kv_block;
 };
 
-size_t attn_bwd_workspace_bytes(int B, int Hq, int L);
+// Q-side tiles one workgroup of the key-major pass takes before a column is
+// shared: a column longer than that (keys every query sees, such as attention
+// sinks or a prefix) would otherwise set the length of the whole pass.
+constexpr int kBwdChunkTiles = 128;
+
+// Key-major split bound and workspace bytes for these sizes (see attn_bwd.hip).
+int bwd_kv_splits(int group, int nQB, int q_block);
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int S, int D, int q_block, int kv_block, int nQB,
+                                int nKB);
 
 hipError_t launch_attn_bwd_bf16_d64(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream);

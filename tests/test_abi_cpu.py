@@ -266,7 +266,7 @@ class Bwd(Fwd):
         self.dout = self.dq = self.dk = self.dv = FAKE
         self.bmq = _bmq(self.L, self.S, self.bm.q_block, self.bm.kv_block)
         self.ws = FAKE
-        self.ws_bytes = 2 * self.B * self.Hq * (-(-self.L // 128) * 128) * 4
+        self.ws_bytes = 2 * self.B * self.Hq * (-(-self.L // 128) * 128) * 4    # columns too short to share
 
     def call(self, lib):
         a3 = lambda x: None if x is None else (ctypes.c_int64 * 3)(*x)
@@ -310,11 +310,22 @@ def test_bwd_valid_call_reaches_the_launch(lib):
 
 
 def test_bwd_workspace_bytes(lib):
+    ws = lambda B, Hq, Hkv, L, S, D, bm, dtype=1: lib.flex_attn_bwd_workspace_bytes(dtype, B, Hq, Hkv, L, S, D,
+                                                                                    ctypes.byref(bm))
     # two float32 per (batch, query head, row), rows padded to a multiple of 128
-    assert lib.flex_attn_bwd_workspace_bytes(2, 3, 100) == 2 * 2 * 3 * 128 * 4
-    assert lib.flex_attn_bwd_workspace_bytes(1, 1, 129) == 2 * 256 * 4
-    assert lib.flex_attn_bwd_workspace_bytes(0, 1, 10) == 0
-    assert lib.flex_attn_bwd_workspace_bytes(1, 1, 0) == 0
+    assert ws(2, 3, 3, 100, 100, 64, _bm(100, 100, 128, 64)) == 2 * 2 * 3 * 128 * 4
+    assert ws(1, 1, 1, 129, 129, 64, _bm(129, 129, 64, 64)) == 2 * 256 * 4
+    # columns of up to 4 * 64 * 2 = 512 Q-side tiles may be shared by up to four
+    # workgroups: four float32 (dk, dv) partials per 64-key column
+    L = S = 8192
+    cols = 2 * 2 * (S // 64)
+    assert ws(2, 8, 2, L, S, 128, _bm(L, S, 128, 64)) == 2 * 2 * 8 * L * 4 + 4 * cols * 2 * 64 * 128 * 4
+    assert ws(0, 1, 1, 10, 10, 64, _bm(10, 10, 64, 64)) == 0
+    assert ws(1, 1, 1, 0, 10, 64, _bm(10, 10, 64, 64)) == 0
+    assert ws(1, 4, 3, 10, 10, 64, _bm(10, 10, 64, 64)) == 0              # not a GQA ratio
+    assert ws(1, 1, 1, 10, 10, 96, _bm(10, 10, 64, 64)) == 0              # head dim
+    assert ws(1, 1, 1, 10, 10, 64, _bm(10, 10, 32, 64)) == 0              # q_block
+    assert lib.flex_attn_bwd_workspace_bytes(1, 1, 1, 1, 10, 10, 64, None) == 0
 
 
 def test_transpose_rejects(lib):

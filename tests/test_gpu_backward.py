@@ -248,3 +248,14 @@ class ScoreModAt:
 
     def __call__(self, s, b, h, q_pos, kv, heads):
         return self.mod(s, b, self.h, q_pos, kv, self.heads)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_bwd_long_columns_split(dev, dtype, D):
+    """Columns longer than one workgroup's share: eight query heads per K/V
+    head and nine 128-row Q blocks give up to 144 Q-side tiles per 64-key
+    column, so the key-major pass splits columns and adds the partial sums
+    (every column under the no-op mask, the sink column under the window)."""
+    for mask in (dict(mask_kind="noop"), dict(mask_kind="causal_window_sinks", window=100, sinks=4)):
+        run_bwd_case(dev, seed=60 + D, dtype=dtype, B=1, Hq=8, Hkv=1, L=1100, S=1100, D=D, qb=128, kb=64,
+                     score=dict(kind="softcap", cap=20.0), what=f"split {dtype} D={D} {mask['mask_kind']}", **mask)
