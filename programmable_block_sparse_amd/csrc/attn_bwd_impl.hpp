@@ -87,41 +87,101 @@ template <typename T, int D> struct BwdOccupancy {
 
 // Per-head constants of the score rule, base-2 units.
 struct BwdConsts {
-    float mul;      // NONE / ALIBI: scale*log2e; soft-cap kinds: 2*scale*log2e/cap
-    float c2;       // cap*log2e
+    ScoreConsts sc;   // mul (NONE / ALIBI: scale*log2e; soft-cap: 2*scale*log2e/cap), c2 = cap*log2e, polynomials
     float scale;
-    float alpha2;   // distance-bias slope * log2e of the query head (0 without bias)
+    float gk;         // scale / c2^2: g'(s) * scale = scale - gk * (capped base-2 score)^2
+    float alpha2;     // distance-bias slope * log2e of the query head (0 without bias)
 };
 
 __device__ __forceinline__ BwdConsts bwd_consts(const BwdArgs& a, int hq) {
     BwdConsts c;
-    c.mul = a.mul;
-    c.c2 = a.c2;
+    c.sc = a.sc;
     c.scale = a.scale;
+    c.gk = a.scale / (a.sc.c2 * a.sc.c2);
     c.alpha2 = 0.0f;
     if (a.score_kind == SCORE_SOFTCAP_ALIBI || a.score_kind == SCORE_ALIBI)
         c.alpha2 = __builtin_amdgcn_exp2f(-(a.alibi_m * (float)(hq + 1)) / (float)a.Hq) * kLog2e;
     return c;
 }
 
-// Base-2 score z2 = g(s) * log2e of accumulator acc (= q.k) plus the bias term
-// bias2 (base-2 distance bias, used by the ALiBi kinds), and gs = g'(s) * scale.
-// The soft-cap tanh is evaluated as 1 - 2 / (1 + e^{2y}), exact in the limits.
-template <int SCORE>
-__device__ __forceinline__ float score2(float acc, float bias2, const BwdConsts& c, float& gs) {
-    if constexpr (SCORE == SCORE_NONE) {
-        gs = c.scale;
-        return acc * c.mul;
-    } else if constexpr (SCORE == SCORE_ALIBI) {
-        gs = c.scale;
-        return __builtin_fmaf(acc, c.mul, bias2);
+// Base-2 scores z[r] = g(s) * log2e of the accumulators s[r] (= q.k) plus the
+// distance bias bias0 + step * acc_row(r, 0) (ALiBi kinds), and gs[r] =
+// g'(s) * scale.  The soft-cap tanh uses the forward's polynomials when every
+// |s| of the wave is in their range (wave-uniform choice; their error, at
+// most 7.9e-6 of the cap, is far inside the bf16 bounds), else the exact form
+// cap - 2 cap / (1 + e^{2y}); the fp32 path always takes the exact form.
+template <int SCORE, bool PRECISE>
+__device__ __forceinline__ void scores2(const f32x16_t& s, float bias0, float step, const BwdConsts& c, float (&z)[16],
+                                        float (&gs)[16]) {
+    constexpr bool kBias = SCORE == SCORE_ALIBI || SCORE == SCORE_SOFTCAP_ALIBI;
+    auto bias = [&](int r) __attribute__((always_inline)) {
+        return kBias ? __builtin_fmaf(step, (float)acc_row(r, 0), bias0) : 0.0f;
+    };
+    if constexpr (SCORE == SCORE_NONE || SCORE == SCORE_ALIBI) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            z[r] = kBias ? __builtin_fmaf(s[r], c.sc.mul, bias(r)) : s[r] * c.sc.mul;
+            gs[r] = c.scale;
+        }
+        return;
     } else {
-        const float e = __builtin_amdgcn_exp2f(acc * c.mul);
-        const float r = __builtin_amdgcn_rcpf(1.0f + e);
-        const float t = __builtin_fmaf(-2.0f, r, 1.0f);
-        gs = __builtin_fmaf(-t * c.scale, t, c.scale);
-        if constexpr (SCORE == SCORE_SOFTCAP_ALIBI) return __builtin_fmaf(t, c.c2, bias2);
-        else return t * c.c2;
+        int tier = 2;   // 0 cubic, 1 quintic, 2 exact
+        if constexpr (!PRECISE) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(s[r]));
+            tier = !__any(amax > c.sc.amax1) ? 0 : (!__any(amax > c.sc.amax) ? 1 : 2);
+        }
+        if (tier == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = s[r] * __builtin_fmaf(s[r] * s[r], c.sc.j1, c.sc.j0);
+        } else if (tier == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float w = s[r] * s[r];
+                z[r] = s[r] * __builtin_fmaf(w, __builtin_fmaf(w, c.sc.k2, c.sc.k1), c.sc.k0);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(s[r] * c.sc.mul);
+                z[r] = __builtin_fmaf(-2.0f * c.sc.c2, __builtin_amdgcn_rcpf(1.0f + e), c.sc.c2);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            gs[r] = __builtin_fmaf(-c.gk * z[r], z[r], c.scale);
+            if constexpr (kBias) z[r] += bias(r);
+        }
+    }
+}
+
+// S and dP blocks of one 32-row block of two LDS tiles against two register
+// operands (bf16), with the two MFMA chains interleaved so neither waits on
+// its own previous result.
+template <int D>
+__device__ __forceinline__ void qk2_block_bf16(const QRegs<__bf16, D>& ra, const QRegs<__bf16, D>& rb,
+                                               const char* __restrict__ ta, const char* __restrict__ tb,
+                                               const LdsAddr<__bf16, D>& la, f32x16_t& sa, f32x16_t& sb) {
+    sa = f32x16_t{};
+    sb = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(ta + la.k[s]);
+        const bf16x8_t xb = *reinterpret_cast<const bf16x8_t*>(tb + la.k[s]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, ra.x[s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, rb.x[s], sb, 0, 0, 0);
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void qk2_block(const QRegs<T, D>& ra, const QRegs<T, D>& rb, const char* ta, const char* tb,
+                                          const LdsAddr<T, D>& la, int kb2, int lane, f32x16_t& sa, f32x16_t& sb) {
+    if constexpr (sizeof(T) == 2) {
+        qk2_block_bf16<D>(ra, rb, ta, tb, la, sa, sb);
+    } else {
+        sa = qk_block<T, D>(ra, ta, la, kb2, lane);
+        sb = qk_block<T, D>(rb, tb, la, kb2, lane);
     }
 }
 
@@ -476,45 +536,33 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
 
         auto compute = [&](const char* cur, int q0, bool masked) __attribute__((always_inline)) {
             const int qr0 = q0 + 32 * qh + 4 * hf;
-            const uint32_t keep =
-                masked ? mask_bits_keys<EXT>(a.mask, key, a.S, a.L, qr0, hq, doc_k,
-                                             reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf)
-                       : ~0u;
+            f32x16_t s, dp;
+            qk2_block<T, D>(kr, vr, cur, cur + G::kTileBytes, la, kb2, lane, s, dp);
+            float z[16], pg[16];
+            scores2<SCORE, Precise<T>::value>(s, bc.alpha2 * (float)(key - (qr0 + a.mask.q_offset)), -bc.alpha2, bc,
+                                              z, pg);
+            if (masked) {
+                const uint32_t keep =
+                    mask_bits_keys<EXT>(a.mask, key, a.S, a.L, qr0, hq, doc_k,
+                                        reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) z[r] = (keep >> acc_row(r, 0)) & 1u ? z[r] : kNegInf;
+            }
+            // P = exp2(z - lse2) and dS = P (dP - D) g' scale, per row of the block
             const float* st = reinterpret_cast<const float*>(cur + G::kStatsOffset) + 32 * qh + 4 * hf;
-            const float bias0 = bc.alpha2 * (float)(key - (qr0 + a.mask.q_offset));
-            // head dim 64: both score-shaped products first (independent MFMA
-            // work to overlap with the exponentials); head dim 128: dP after
-            // the dV product, so fewer registers are live at once
-            const f32x16_t s = qk_block<T, D>(kr, cur, la, kb2, lane);
-            f32x16_t dp;
-            if constexpr (D == 64) dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
-            float p[16], pg[16];   // P, and P * g'(s) * scale
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const float4 l4 = *reinterpret_cast<const float4*>(st + 8 * gq);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * gq + e;
-                    float gs;
-                    float z = score2<SCORE>(s[r], __builtin_fmaf(-bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs);
-                    z = (keep >> acc_row(r, 0)) & 1u ? z : kNegInf;
-                    p[r] = __builtin_amdgcn_exp2f(z - lv[e]);
-                    pg[r] = p[r] * gs;
-                }
-            }
-            xtp<T, D>(dv, p, cur + G::kTileBytes, la, kb2, lane);   // dv^T += dO^T P
-            if constexpr (D != 64) dp = qk_block<T, D>(vr, cur + G::kTileBytes, la, kb2, lane);
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
                 const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 8 * gq);
-                const float dsv[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dsv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * gq + e;
-                    pg[r] *= dp[r] - dsv[e];                              // dS
+                    z[r] = __builtin_amdgcn_exp2f(z[r] - lv[e]);
+                    pg[r] *= z[r] * (dp[r] - dsv[e]);
                 }
             }
+            xtp<T, D>(dv, z, cur + G::kTileBytes, la, kb2, lane);   // dv^T += dO^T P
             xtp<T, D>(dk, pg, cur, la, kb2, lane);                 // dk^T += Q^T dS
         };
 
@@ -744,21 +792,14 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     };
 
     auto compute = [&](const char* cur, int kv0, bool masked) __attribute__((always_inline)) {
-        const f32x16_t s = qk_block<T, D>(qr, cur, la, kb2, lane);
-        const f32x16_t dp = qk_block<T, D>(dor, cur + G::kTileBytes, la, kb2, lane);
+        f32x16_t s, dp;
+        qk2_block<T, D>(qr, dor, cur, cur + G::kTileBytes, la, kb2, lane, s, dp);
         const int key_base = kv0 + 32 * kh + 4 * hf;
-        const float bias0 = bc.alpha2 * (float)(key_base - row.q_pos);
-        float z[16], gs[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            z[r] = score2<SCORE>(s[r], __builtin_fmaf(bc.alpha2, (float)acc_row(r, 0), bias0), bc, gs[r]);
+        float z[16], ds[16];
+        scores2<SCORE, Precise<T>::value>(s, bc.alpha2 * (float)(key_base - row.q_pos), bc.alpha2, bc, z, ds);
         if (masked) apply_mask<EXT>(z, a.mask, kv0, a.S, row, reinterpret_cast<const int*>(cur + G::kDocOffset), kh, hf);
-        float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(z[r] - lse2);
-            ds[r] = p * (dp[r] - dsum) * gs[r];
-        }
+        for (int r = 0; r < 16; ++r) ds[r] *= __builtin_amdgcn_exp2f(z[r] - lse2) * (dp[r] - dsum);
         xtp<T, D>(dq, ds, cur, la, kb2, lane);   // dq^T += K^T dS^T
     };
 

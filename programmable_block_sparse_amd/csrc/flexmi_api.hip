@@ -453,9 +453,7 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
     a.score_kind = score->kind;
     a.alibi_m = score->alibi_m;
     const bool capped = score->kind == FLEX_SCORE_SOFTCAP || score->kind == FLEX_SCORE_SOFTCAP_ALIBI;
-    const double l2e = 1.4426950408889634;
-    a.mul = capped ? (float)(2.0 * (double)a.scale * l2e / (double)score->cap) : (float)((double)a.scale * l2e);
-    a.c2 = capped ? (float)((double)score->cap * l2e) : 0.0f;
+    a.sc = score_consts(a.scale, capped ? score->cap : 1.0f, score->kind);
     a.mask = to_mask_args(mask);
     a.kv_num = bm->kv_num_blocks;
     a.kv_idx = bm->kv_indices;

@@ -137,8 +137,7 @@ struct BwdArgs {
     float scale;
     int score_kind;
     float alibi_m;
-    float mul;          // NONE / ALIBI: scale*log2e; soft-cap kinds: 2*scale*log2e/cap
-    float c2;           // cap*log2e
+    ScoreConsts sc;     // base-2 constants of the score rule (as for the forward)
     MaskArgs mask;
     const int* kv_num;  // KV-side lists (the query-major pass)
     const int* kv_idx;
