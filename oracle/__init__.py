@@ -12,7 +12,8 @@ Contents
               -inf mask, then a row softmax (also how the pages describe the
               unfused fallback)
   blockmask   tile classification by counting visible cells, ordered lists,
-              to_dense / sparsity helpers, the Q-side (transposed) lists
+              to_dense / sparsity helpers, the Q-side (transposed) lists, and the
+              BlockMask utilities (slicing, cropping, the ASCII picture)
   blockwise   a second, independent float64 oracle that walks only the block
               lists with an online softmax; used to show the block mask loses
               nothing
@@ -25,12 +26,14 @@ only say must be checked separately.
 """
 from .mods import ScoreMod, MaskMod, alibi_slope
 from .attention import attention, attention_rows
-from .blockmask import build_block_mask, to_dense, sparsity, visible_cells, transpose_block_mask
+from .blockmask import (build_block_mask, to_dense, sparsity, visible_cells, transpose_block_mask,
+                        slice_block_mask, adjust_block_mask, grid_classes, to_string)
 from .blockwise import blockwise_attention
 from .backward import attention_backward, score_derivative
 
 __all__ = [
     "ScoreMod", "MaskMod", "alibi_slope", "attention", "attention_rows",
     "build_block_mask", "to_dense", "sparsity", "visible_cells", "blockwise_attention",
-    "transpose_block_mask", "attention_backward", "score_derivative",
+    "transpose_block_mask", "slice_block_mask", "adjust_block_mask", "grid_classes", "to_string",
+    "attention_backward", "score_derivative",
 ]

@@ -143,3 +143,90 @@ def transpose_block_mask(bm: dict) -> dict:
                     cnt[b, h, kb], idx[b, h, kb] = _ordered(member[b, h, kb])
         out[tnum], out[tind] = cnt, idx
     return out
+
+
+def slice_block_mask(bm: dict, batches=None, heads=None, rows=None) -> dict:
+    """BlockMask restricted to batch range ``batches``, head range ``heads`` and
+    Q-block rows ``rows`` (each a (start, stop) pair, default all).
+
+    The 2kiu guide, section 3.3 (__getitem__): up to three indices select
+    batch, head and Q-block row (a row of the tile grid, not a query token);
+    integer indices become length-1 ranges so the dimensions stay.
+    """
+    B, H, nQB, nKB = bm["kv_indices"].shape
+    b0, b1 = batches or (0, B)
+    h0, h1 = heads or (0, H)
+    r0, r1 = rows or (0, nQB)
+    out = {name: np.array(bm[name][b0:b1, h0:h1, r0:r1], dtype=np.int32)
+           for name in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices")}
+    out.update(q_block=bm["q_block"], kv_block=bm["kv_block"])
+    return out
+
+
+def adjust_block_mask(bm: dict, new_L: int, new_S: int) -> dict:
+    """Crop a BlockMask to the top-left new lengths (2kiu guide, section 3.3, _adjust).
+
+    Reading (the page gives the intent only, and warns it does not hold for
+    every mask_mod): keep the first ceil(new_L / q_block) Q-block rows and,
+    in each, the listed KV blocks below ceil(new_S / kv_block), in their
+    order; a tile that now covers cells past new_L or new_S cannot be full
+    (cells past the lengths are not visible), so such a full tile becomes
+    partial.  Lists are then completed as the builder completes them.
+    """
+    qb, kb = bm["q_block"], bm["kv_block"]
+    nq, nk = _ceil_div(new_L, qb), _ceil_div(new_S, kb)
+    cls = tile_classes(bm)[:, :, :nq, :nk].copy()
+    if new_L % qb:
+        cls[:, :, nq - 1, :][cls[:, :, nq - 1, :] == "F"] = "P"
+    if new_S % kb:
+        cls[:, :, :, nk - 1][cls[:, :, :, nk - 1] == "F"] = "P"
+    B, H = cls.shape[:2]
+    out = {"kv_num_blocks": np.zeros((B, H, nq), np.int32), "kv_indices": np.zeros((B, H, nq, nk), np.int32),
+           "full_kv_num_blocks": np.zeros((B, H, nq), np.int32),
+           "full_kv_indices": np.zeros((B, H, nq, nk), np.int32), "q_block": qb, "kv_block": kb}
+    for b in range(B):
+        for h in range(H):
+            for r in range(nq):
+                out["kv_num_blocks"][b, h, r], out["kv_indices"][b, h, r] = _ordered(cls[b, h, r] == "P")
+                out["full_kv_num_blocks"][b, h, r], out["full_kv_indices"][b, h, r] = _ordered(cls[b, h, r] == "F")
+    return out
+
+
+def grid_classes(bm: dict, grid_rows: int, grid_cols: int) -> np.ndarray:
+    """Tile classes pooled into windows: 2 where every tile of the window is
+    full, 0 where every tile is empty, 1 otherwise.
+
+    Windows are ceil(nQB / grid_rows) x ceil(nKB / grid_cols) tiles (the last
+    ones cut), so a grid no smaller than the tile grid is the tile grid
+    itself.  This is the picture the 2kiu guide's to_string draws (section
+    3.3: full, partial and empty blocks, grid_size bounding the picture); how
+    it compresses a larger grid the page leaves open, and pooling by window is
+    this oracle's reading.
+    """
+    cls = tile_classes(bm)
+    B, H, nQB, nKB = cls.shape
+    wr, wc = _ceil_div(nQB, grid_rows), _ceil_div(nKB, grid_cols)
+    out = np.zeros((B, H, _ceil_div(nQB, wr), _ceil_div(nKB, wc)), dtype=np.int8)
+    for i in range(out.shape[2]):
+        for j in range(out.shape[3]):
+            win = cls[:, :, i * wr:(i + 1) * wr, j * wc:(j + 1) * wc]
+            all_full = (win == "F").all(axis=(2, 3))
+            all_empty = (win == "0").all(axis=(2, 3))
+            out[:, :, i, j] = np.where(all_full, 2, np.where(all_empty, 0, 1))
+    return out
+
+
+def to_string(bm: dict, grid_rows: int = 20, grid_cols: int = 20, limit: int = 4) -> str:
+    """ASCII picture of the first ``limit`` (batch, head) grids: '█' full,
+    '░' partial, ' ' empty (2kiu guide, section 3.3, to_string)."""
+    g = grid_classes(bm, grid_rows, grid_cols)
+    chars = {0: " ", 1: "░", 2: "█"}
+    parts, shown = [], 0
+    for b in range(g.shape[0]):
+        for h in range(g.shape[1]):
+            if shown == limit:
+                break
+            parts.append(f"b={b} h={h}")
+            parts.extend("".join(chars[int(c)] for c in row) for row in g[b, h])
+            shown += 1
+    return "\n".join(parts)
