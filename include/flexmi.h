@@ -288,6 +288,55 @@ typedef struct {
  * Errors: NULL, BLOCKMASK (dims differ or out of range), HIP. */
 flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block_mask_q* bmq, void* stream);
 
+/* BlockMask utilities (2kiu guide, section 3.3).  Each reads a BlockMask as
+ * flex_blockmask_build writes it (counts clamped to [0, num_kv_blocks]; a block
+ * in both lists counts as partial, a block listed twice once) and writes
+ * caller-allocated device memory; at most 65536 KV blocks per row.
+ * Errors: NULL, BLOCKMASK (dims or ranges), UNSUPPORTED, HIP. */
+
+/* to_dense: dense[b][h][qb][kb] = 1 where the lists name tile (qb, kb), as
+ * partial or full, else 0 (int32, B*H*num_q_blocks*num_kv_blocks entries; the
+ * row-wise rebuild of the guide's section 3.2). */
+flex_status flex_blockmask_to_dense(const flex_block_mask* bm, int32_t* dense, void* stream);
+
+/* The picture to_string draws: tile classes pooled into windows of
+ * wr = ceil(num_q_blocks / grid_rows) by wc = ceil(num_kv_blocks / grid_cols)
+ * tiles (the last ones cut); grid[b][h][i][j] = 2 when every tile of window
+ * (i, j) is full, 0 when every tile is empty, 1 otherwise.  int8 device array
+ * of B*H*ceil(num_q_blocks / wr)*ceil(num_kv_blocks / wc) entries; grid_rows,
+ * grid_cols >= 1 (a grid no smaller than the tile grid gives the tile
+ * classes themselves). */
+flex_status flex_blockmask_grid(const flex_block_mask* bm, int32_t grid_rows, int32_t grid_cols, int8_t* grid,
+                                void* stream);
+
+/* sparsity: 100 * (1 - listed tiles / all tiles) over the whole
+ * B x H x num_q_blocks x num_kv_blocks grid, written as one double to device
+ * memory `percent` (8-byte aligned; also used as the counter while the call
+ * runs). */
+flex_status flex_blockmask_sparsity(const flex_block_mask* bm, double* percent, void* stream);
+
+/* __getitem__: the rows of batches [r[0], r[1]), heads [r[2], r[3]) and Q-block
+ * rows [r[4], r[5]) (ranges non-empty and inside the dims; the third range
+ * indexes rows of the tile grid, not query tokens).  out: B = r[1]-r[0],
+ * H = r[3]-r[2], num_q_blocks = r[5]-r[4], the same block sizes and
+ * num_kv_blocks, and four caller-allocated arrays.  The slice serves queries
+ * r[4]*q_block onwards, with the logical position q_offset + r[4]*q_block for
+ * its first row. */
+flex_status flex_blockmask_slice(const flex_block_mask* bm, const int32_t ranges[6], const flex_block_mask* out,
+                                 void* stream);
+
+/* _adjust: crop to the top-left lengths new_L x new_S, with
+ * ceil(new_L / q_block) <= num_q_blocks and ceil(new_S / kv_block) <=
+ * num_kv_blocks.  Each kept row keeps its listed blocks below the new column
+ * count, in order; a full tile that now reaches past new_L or new_S becomes
+ * partial (cells past the lengths are not visible).  The result equals a
+ * rebuild when the cut falls on tile boundaries and the mask does not depend
+ * on the lengths; otherwise it is conservative: every tile a rebuild would
+ * visit is visited, and a tile is skipped its element mask only if a rebuild
+ * would call it full.  out: dims for the new lengths and four arrays. */
+flex_status flex_blockmask_adjust(const flex_block_mask* bm, int64_t new_L, int64_t new_S, const flex_block_mask* out,
+                                  void* stream);
+
 /* Bytes of device workspace flex_attn_bwd needs for these sizes: per (batch,
  * query head, row, rows padded to a multiple of 128) the base-2 lse and
  * D_i = dO_i . O_i as float32, plus, when one KV block's Q-side tiles may be

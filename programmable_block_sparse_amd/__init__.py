@@ -12,6 +12,8 @@ the same names:
   flex_blockmask_transpose(block_mask) -> BlockMaskQ
   flex_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
   flex_attn_bwd_workspace_bytes(...)
+  BlockMask.to_dense / grid / to_string / sparsity / [b, h, rows] / adjust
+      (flex_blockmask_to_dense, _grid, _sparsity, _slice, _adjust)
   flex_status_string(code)
 
 There is no fallback: if the native library is missing or cannot load, every
@@ -42,6 +44,8 @@ MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
                     "flex_blockmask_transpose", "flex_attn_bwd_workspace_bytes", "flex_attn_bwd",
+                    "flex_blockmask_to_dense", "flex_blockmask_grid", "flex_blockmask_sparsity",
+                    "flex_blockmask_slice", "flex_blockmask_adjust",
                     "flex_status_string", "flex_last_error")
 
 
@@ -119,6 +123,15 @@ def load_library():
                                   ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P, P, P, P,
                                   ctypes.c_size_t, P]
     lib.flex_attn_bwd.restype = ctypes.c_int
+    BMP = ctypes.POINTER(flex_block_mask)
+    lib.flex_blockmask_to_dense.argtypes = [BMP, P, P]
+    lib.flex_blockmask_grid.argtypes = [BMP, I32, I32, P, P]
+    lib.flex_blockmask_sparsity.argtypes = [BMP, P, P]
+    lib.flex_blockmask_slice.argtypes = [BMP, ctypes.POINTER(ctypes.c_int32), BMP, P]
+    lib.flex_blockmask_adjust.argtypes = [BMP, I64, I64, BMP, P]
+    for name in ("flex_blockmask_to_dense", "flex_blockmask_grid", "flex_blockmask_sparsity", "flex_blockmask_slice",
+                 "flex_blockmask_adjust"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.flex_status_string.argtypes = [I32]
     lib.flex_status_string.restype = ctypes.c_char_p
     lib.flex_last_error.argtypes = []
@@ -229,6 +242,114 @@ class BlockMask:
     @property
     def H(self) -> int:
         return self.kv_num_blocks.shape[1]
+
+    # -- utilities of the 2kiu guide, section 3.3 (each runs in a library kernel)
+    @property
+    def shape(self):
+        """batch dims + sequence lengths: (B, H, L, S)."""
+        return (self.B, self.H, self.L, self.S)
+
+    def numel(self) -> int:
+        """Elements of the mask, sparse ones included."""
+        return self.B * self.H * self.L * self.S
+
+    def _empty_like(self, B, H, nqb, nkb, L, S) -> "BlockMask":
+        dev = self.kv_indices.device
+        t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+        return BlockMask(t(B, H, nqb), t(B, H, nqb, nkb), t(B, H, nqb), t(B, H, nqb, nkb), self.q_block,
+                         self.kv_block, L, S)
+
+    def to_dense(self) -> torch.Tensor:
+        """int32 (B, H, nQB, nKB): 1 where a tile is computed (C: flex_blockmask_to_dense)."""
+        dense = torch.empty(self.kv_indices.shape, dtype=torch.int32, device=self.kv_indices.device)
+        _check(load_library().flex_blockmask_to_dense(ctypes.byref(self.to_c()), dense.data_ptr(), self._stream()))
+        return dense
+
+    def grid(self, grid_rows: int, grid_cols: int) -> torch.Tensor:
+        """int8 tile classes pooled into windows: 2 all full, 0 all empty, 1 mixed (C: flex_blockmask_grid)."""
+        B, H, nqb, nkb = self.kv_indices.shape
+        wr, wc = -(-nqb // grid_rows), -(-nkb // grid_cols)
+        out = torch.empty((B, H, -(-nqb // wr), -(-nkb // wc)), dtype=torch.int8, device=self.kv_indices.device)
+        _check(load_library().flex_blockmask_grid(ctypes.byref(self.to_c()), grid_rows, grid_cols, out.data_ptr(),
+                                                  self._stream()))
+        return out
+
+    def to_string(self, grid_size=(20, 20), limit: int = 4) -> str:
+        """ASCII picture: '█' full, '░' partial, ' ' empty; grid_size=-1 draws every tile."""
+        B, H, nqb, nkb = self.kv_indices.shape
+        gr, gc = (nqb, nkb) if grid_size == -1 else grid_size
+        g = self.grid(gr, gc).cpu().numpy()
+        glyph = {0: " ", 1: "░", 2: "█"}
+        lines, shown = [], 0
+        for b in range(B):
+            for h in range(H):
+                if shown == limit:
+                    break
+                lines.append(f"b={b} h={h}")
+                lines.extend("".join(glyph[int(c)] for c in row) for row in g[b, h])
+                shown += 1
+        return "\n".join(lines)
+
+    def sparsity(self) -> float:
+        """Percentage of tiles not computed (C: flex_blockmask_sparsity; waits for the result)."""
+        out = torch.empty(1, dtype=torch.float64, device=self.kv_indices.device)
+        _check(load_library().flex_blockmask_sparsity(ctypes.byref(self.to_c()), out.data_ptr(), self._stream()))
+        return float(out.item())
+
+    def __getitem__(self, index) -> "BlockMask":
+        """Select batches, heads and Q-block rows (integers keep their dimension) (C: flex_blockmask_slice)."""
+        if not isinstance(index, tuple):
+            index = (index,)
+        if len(index) > 3:
+            raise IndexError("at most three indices: batch, head, Q-block row")
+        B, H, nqb, nkb = self.kv_indices.shape
+        ranges = []
+        for i, n in zip(range(3), (B, H, nqb)):
+            sel = index[i] if i < len(index) else slice(None)
+            if isinstance(sel, int):
+                sel = slice(sel % n, sel % n + 1) if -n <= sel < n else None
+            if sel is None or not isinstance(sel, slice) or sel.step not in (None, 1):
+                raise IndexError(f"index {index[i]!r} is not a unit-step range inside {n}")
+            start, stop, _ = sel.indices(n)
+            ranges.append((start, stop))
+        (b0, b1), (h0, h1), (r0, r1) = ranges
+        rows_L = max(0, min(self.L - r0 * self.q_block, (r1 - r0) * self.q_block))
+        out = self._empty_like(b1 - b0, h1 - h0, r1 - r0, nkb, rows_L, self.S)
+        arr = (ctypes.c_int32 * 6)(b0, b1, h0, h1, r0, r1)
+        _check(load_library().flex_blockmask_slice(ctypes.byref(self.to_c()), arr, ctypes.byref(out.to_c()),
+                                                   self._stream()))
+        return out
+
+    def adjust(self, new_L: int, new_S: int) -> "BlockMask":
+        """Crop to the top-left new lengths (C: flex_blockmask_adjust)."""
+        B, H = self.B, self.H
+        out = self._empty_like(B, H, -(-new_L // self.q_block), -(-new_S // self.kv_block), new_L, new_S)
+        _check(load_library().flex_blockmask_adjust(ctypes.byref(self.to_c()), new_L, new_S, ctypes.byref(out.to_c()),
+                                                    self._stream()))
+        return out
+
+    _adjust = adjust
+
+    def as_tuple(self):
+        """The four arrays followed by (q_block, kv_block, L, S)."""
+        return (self.kv_num_blocks, self.kv_indices, self.full_kv_num_blocks, self.full_kv_indices, self.q_block,
+                self.kv_block, self.L, self.S)
+
+    @classmethod
+    def from_kv_blocks(cls, kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices, *, q_block: int,
+                       kv_block: int, L: int, S: int) -> "BlockMask":
+        """Wrap existing KV-side lists (int32 device tensors, (B, H, nQB[, nKB]))."""
+        for t in (kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("block lists must be contiguous int32 tensors")
+        return cls(kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices, q_block, kv_block, L, S)
+
+    def to(self, device) -> "BlockMask":
+        """A copy on another device (this mask is unchanged)."""
+        return BlockMask(*(t.to(device) for t in self.as_tuple()[:4]), self.q_block, self.kv_block, self.L, self.S)
+
+    def _stream(self):
+        return ctypes.c_void_p(_stream_ptr(self.kv_indices.device))
 
     def to_c(self) -> flex_block_mask:
         cached = self.__dict__.get("_c")

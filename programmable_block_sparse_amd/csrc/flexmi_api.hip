@@ -145,6 +145,44 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
+namespace {
+
+flex_status check_util_bm(const flex_block_mask* bm) {
+    if (!bm) return fail(FLEX_ERR_NULL, "bm must not be NULL");
+    if (flex_status s = check_bm_arrays(bm)) return s;
+    if (bm->B < 1 || bm->H < 1 || bm->num_q_blocks < 1 || bm->num_kv_blocks < 1 || bm->q_block < 1 ||
+        bm->kv_block < 1 || bm->B > 65535 || bm->H > 65535)
+        return fail(FLEX_ERR_BLOCKMASK, "block mask dims out of range");
+    if (bm->num_kv_blocks > 65536)
+        return fail(FLEX_ERR_UNSUPPORTED, "at most 65536 KV blocks per row (got %d)", bm->num_kv_blocks);
+    if ((int64_t)bm->B * bm->H * bm->num_q_blocks >= (int64_t(1) << 31) ||
+        (int64_t)bm->B * bm->H * bm->num_q_blocks * bm->num_kv_blocks >= (int64_t(1) << 40))
+        return fail(FLEX_ERR_UNSUPPORTED, "block mask too large");
+    return FLEX_OK;
+}
+
+UtilArgs util_args(const flex_block_mask* bm) {
+    UtilArgs a;
+    a.kv_num = bm->kv_num_blocks;
+    a.kv_idx = bm->kv_indices;
+    a.full_num = bm->full_kv_num_blocks;
+    a.full_idx = bm->full_kv_indices;
+    a.Bm = bm->B;
+    a.Hm = bm->H;
+    a.nQB = bm->num_q_blocks;
+    a.nKB = bm->num_kv_blocks;
+    return a;
+}
+
+UtilOut util_out(const flex_block_mask* o) { return UtilOut{o->kv_num_blocks, o->kv_indices, o->full_kv_num_blocks, o->full_kv_indices}; }
+
+flex_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FLEX_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return FLEX_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* flex_status_string(int32_t s) {
@@ -473,6 +511,74 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
     hipError_t e = launch_attn_bwd(dtype, D, a, as_stream(stream));
     if (e != hipSuccess) return fail(FLEX_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return FLEX_OK;
+}
+
+flex_status flex_blockmask_to_dense(const flex_block_mask* bm, int32_t* dense, void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_util_bm(bm)) return s;
+    if (!dense) return fail(FLEX_ERR_NULL, "dense must not be NULL");
+    (void)hipGetLastError();
+    return launched(launch_blockmask_to_dense(util_args(bm), dense, as_stream(stream)), "to_dense");
+}
+
+flex_status flex_blockmask_grid(const flex_block_mask* bm, int32_t grid_rows, int32_t grid_cols, int8_t* grid,
+                                void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_util_bm(bm)) return s;
+    if (!grid) return fail(FLEX_ERR_NULL, "grid must not be NULL");
+    if (grid_rows < 1 || grid_cols < 1) return fail(FLEX_ERR_SHAPE, "grid_rows and grid_cols must be >= 1");
+    const int wr = (int)ceil_div(bm->num_q_blocks, grid_rows), wc = (int)ceil_div(bm->num_kv_blocks, grid_cols);
+    (void)hipGetLastError();
+    return launched(launch_blockmask_grid(util_args(bm), wr, wc, grid, as_stream(stream)), "grid");
+}
+
+flex_status flex_blockmask_sparsity(const flex_block_mask* bm, double* percent, void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_util_bm(bm)) return s;
+    if (!percent) return fail(FLEX_ERR_NULL, "percent must not be NULL");
+    if (reinterpret_cast<uintptr_t>(percent) & 7u) return fail(FLEX_ERR_LAYOUT, "percent must be 8-byte aligned");
+    (void)hipGetLastError();
+    return launched(launch_blockmask_sparsity(util_args(bm), percent, as_stream(stream)), "sparsity");
+}
+
+flex_status flex_blockmask_slice(const flex_block_mask* bm, const int32_t ranges[6], const flex_block_mask* out,
+                                 void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_util_bm(bm)) return s;
+    if (!ranges || !out) return fail(FLEX_ERR_NULL, "ranges and out must not be NULL");
+    if (flex_status s = check_bm_arrays(out)) return s;
+    const int32_t* r = ranges;
+    if (r[0] < 0 || r[1] > bm->B || r[0] >= r[1] || r[2] < 0 || r[3] > bm->H || r[2] >= r[3] || r[4] < 0 ||
+        r[5] > bm->num_q_blocks || r[4] >= r[5])
+        return fail(FLEX_ERR_BLOCKMASK, "slice ranges [%d,%d) x [%d,%d) x [%d,%d) are empty or outside %d x %d x %d",
+                    r[0], r[1], r[2], r[3], r[4], r[5], bm->B, bm->H, bm->num_q_blocks);
+    if (out->B != r[1] - r[0] || out->H != r[3] - r[2] || out->num_q_blocks != r[5] - r[4] ||
+        out->num_kv_blocks != bm->num_kv_blocks || out->q_block != bm->q_block || out->kv_block != bm->kv_block)
+        return fail(FLEX_ERR_BLOCKMASK, "out dims do not match the slice");
+    SliceArgs sa{r[0], r[2], r[4], r[1] - r[0], r[3] - r[2], r[5] - r[4]};
+    (void)hipGetLastError();
+    return launched(launch_blockmask_slice(util_args(bm), sa, util_out(out), as_stream(stream)), "slice");
+}
+
+flex_status flex_blockmask_adjust(const flex_block_mask* bm, int64_t new_L, int64_t new_S, const flex_block_mask* out,
+                                  void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_util_bm(bm)) return s;
+    if (!out) return fail(FLEX_ERR_NULL, "out must not be NULL");
+    if (flex_status s = check_bm_arrays(out)) return s;
+    if (new_L < 1 || new_S < 1) return fail(FLEX_ERR_SHAPE, "new lengths must be positive");
+    const int64_t nq = ceil_div(new_L, bm->q_block), nk = ceil_div(new_S, bm->kv_block);
+    if (nq > bm->num_q_blocks || nk > bm->num_kv_blocks)
+        return fail(FLEX_ERR_BLOCKMASK, "cropping to %lld x %lld needs %lld x %lld blocks, the mask has %d x %d",
+                    (long long)new_L, (long long)new_S, (long long)nq, (long long)nk, bm->num_q_blocks,
+                    bm->num_kv_blocks);
+    if (out->B != bm->B || out->H != bm->H || out->q_block != bm->q_block || out->kv_block != bm->kv_block ||
+        out->num_q_blocks != nq || out->num_kv_blocks != nk)
+        return fail(FLEX_ERR_BLOCKMASK, "out dims do not match the cropped lengths");
+    (void)hipGetLastError();
+    return launched(launch_blockmask_adjust(util_args(bm), (int)nq, (int)nk, new_L % bm->q_block != 0,
+                                            new_S % bm->kv_block != 0, util_out(out), as_stream(stream)),
+                    "adjust");
 }
 
 }  // extern "C"

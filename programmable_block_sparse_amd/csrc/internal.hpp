@@ -38,6 +38,33 @@ struct TransposeArgs {
 
 hipError_t launch_blockmask_transpose(const TransposeArgs& a, hipStream_t stream);
 
+// BlockMask utilities (blockmask_utils.hip): input lists, output lists, and
+// the ranges of a slice.
+struct UtilArgs {
+    const int* kv_num;
+    const int* kv_idx;
+    const int* full_num;
+    const int* full_idx;
+    int Bm, Hm, nQB, nKB;
+};
+struct UtilOut {
+    int* kv_num;
+    int* kv_idx;
+    int* full_num;
+    int* full_idx;
+};
+struct SliceArgs {
+    int b0, h0, r0;
+    int batches, heads, rows;
+};
+
+hipError_t launch_blockmask_to_dense(const UtilArgs& a, int32_t* dense, hipStream_t stream);
+hipError_t launch_blockmask_grid(const UtilArgs& a, int wr, int wc, int8_t* grid, hipStream_t stream);
+hipError_t launch_blockmask_sparsity(const UtilArgs& a, double* percent, hipStream_t stream);
+hipError_t launch_blockmask_slice(const UtilArgs& a, const SliceArgs& s, const UtilOut& o, hipStream_t stream);
+hipError_t launch_blockmask_adjust(const UtilArgs& a, int nq, int nk, int edge_row, int edge_col, const UtilOut& o,
+                                   hipStream_t stream);
+
 // Constants of the score rule that depend only on scale and cap (computed on
 // the host in double, rounded once).  Base-2 units: log2(e) is folded in.
 struct ScoreConsts {

@@ -342,3 +342,31 @@ def test_transpose_rejects(lib):
     assert call(bm, bmq) == BLOCKMASK
     bmq = _bmq(256, 300, 128, 64, B=2)
     assert call(bm, bmq) == BLOCKMASK
+
+
+def test_blockmask_utilities_reject(lib):
+    bm = _bm(256, 300, 128, 64, B=2, H=3)
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    assert lib.flex_blockmask_to_dense(ref(bm), FAKE, None) in (OK, HIP)
+    assert lib.flex_blockmask_to_dense(None, FAKE, None) == NULL
+    assert lib.flex_blockmask_to_dense(ref(bm), None, None) == NULL
+    assert lib.flex_blockmask_grid(ref(bm), 0, 4, FAKE, None) == SHAPE
+    assert lib.flex_blockmask_grid(ref(bm), 2, 2, FAKE, None) in (OK, HIP)
+    assert lib.flex_blockmask_sparsity(ref(bm), FAKE + 4, None) == LAYOUT
+    assert lib.flex_blockmask_sparsity(ref(bm), FAKE, None) in (OK, HIP)
+    big = _bm(64, 64 * 70000, 64, 64)
+    assert lib.flex_blockmask_to_dense(ref(big), FAKE, None) == UNSUPPORTED
+    # slicing: ranges inside the dims and non-empty, out dims equal to the ranges
+    r = lambda *v: (ctypes.c_int32 * 6)(*v)
+    out = _bm(128, 300, 128, 64, B=1, H=2)
+    assert lib.flex_blockmask_slice(ref(bm), r(1, 2, 1, 3, 1, 2), ref(out), None) in (OK, HIP)
+    assert lib.flex_blockmask_slice(ref(bm), r(1, 2, 1, 3, 1, 3), ref(out), None) == BLOCKMASK   # rows past nQB
+    assert lib.flex_blockmask_slice(ref(bm), r(1, 1, 1, 3, 1, 2), ref(out), None) == BLOCKMASK   # empty range
+    assert lib.flex_blockmask_slice(ref(bm), r(0, 2, 1, 3, 1, 2), ref(out), None) == BLOCKMASK   # out B differs
+    assert lib.flex_blockmask_slice(ref(bm), None, ref(out), None) == NULL
+    # cropping: only to fewer blocks, out dims for the new lengths
+    adj = _bm(200, 100, 128, 64, B=2, H=3)
+    assert lib.flex_blockmask_adjust(ref(bm), 200, 100, ref(adj), None) in (OK, HIP)
+    assert lib.flex_blockmask_adjust(ref(bm), 200, 400, ref(_bm(200, 400, 128, 64, B=2, H=3)), None) == BLOCKMASK
+    assert lib.flex_blockmask_adjust(ref(bm), 0, 100, ref(adj), None) == SHAPE
+    assert lib.flex_blockmask_adjust(ref(bm), 200, 100, ref(_bm(200, 100, 128, 64)), None) == BLOCKMASK
