@@ -14,7 +14,10 @@ score entering the softmax of each row (-inf for rows with no visible key).
 Grouped-query attention (2kiu guide, section 6.1): query head hq reads K/V
 head hq // (Hq / Hkv).  Query row i has logical position i + q_offset (blog,
 decode section; quant67 article section 4 for the bottom-right alignment
-q_offset = S - L).
+q_offset = S - L).  The same decode section separates a cache's capacity from
+its filled length: with ``kv_len`` a key at or past the valid length is not
+visible whatever the mask says.  ``q_offset`` and ``kv_len`` may be given per
+batch (a sequence indexed by b).
 
 Nothing here is blocked or fused: each row chunk forms the full score row,
 applies g, then the mask, then an ordinary softmax.  Chunking rows only bounds
@@ -43,8 +46,13 @@ def _rows_softmax(z: np.ndarray, vis: np.ndarray, V: np.ndarray):
     return out, lse
 
 
+def _at(value, b):
+    """value[b] for a per-batch sequence, else value."""
+    return value if value is None or np.isscalar(value) else value[b]
+
+
 def attention_rows(q_rows, K, V, *, b: int, hq: int, Hq: int, row_ids, scale: float,
-                   score: ScoreMod, mask: MaskMod, q_offset: int, with_max: bool = False):
+                   score: ScoreMod, mask: MaskMod, q_offset: int, with_max: bool = False, kv_len=None):
     """out (n, D) and lse (n,) for the given query rows of one (batch, query head),
     plus the row maxima of the masked scores when ``with_max``.
 
@@ -60,6 +68,8 @@ def attention_rows(q_rows, K, V, *, b: int, hq: int, Hq: int, row_ids, scale: fl
     kv = np.arange(S, dtype=np.int64)[None, :]
     g = score(s, b, hq, q_pos, kv, Hq)
     vis = mask(b, hq, q_pos, kv)
+    if kv_len is not None:
+        vis = vis & (kv < int(kv_len))
     z = np.where(vis, g, -np.inf)
     out, lse = _rows_softmax(z, vis, V)
     if with_max:
@@ -67,8 +77,8 @@ def attention_rows(q_rows, K, V, *, b: int, hq: int, Hq: int, row_ids, scale: fl
     return out, lse
 
 
-def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int,
-              rows=None, heads=None, batches=None, row_chunk: int = 512, with_max: bool = False):
+def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset,
+              rows=None, heads=None, batches=None, row_chunk: int = 512, with_max: bool = False, kv_len=None):
     """Dense oracle over (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values.
 
     Returns ``out`` (nb, nh, nr, D) and ``lse`` (nb, nh, nr) in float64 for the selected
@@ -95,7 +105,8 @@ def attention(q, k, v, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset
             for c0 in range(0, len(rows), row_chunk):
                 rid = rows[c0:c0 + row_chunk]
                 o, ls, m = attention_rows(q[b, hq][rid], K, V, b=b, hq=hq, Hq=Hq, row_ids=rid,
-                                          scale=scale, score=score, mask=mask, q_offset=q_offset, with_max=True)
+                                          scale=scale, score=score, mask=mask, q_offset=_at(q_offset, b),
+                                          with_max=True, kv_len=_at(kv_len, b))
                 out[bi, hi, c0:c0 + len(rid)] = o
                 lse[bi, hi, c0:c0 + len(rid)] = ls
                 mx[bi, hi, c0:c0 + len(rid)] = m

@@ -51,8 +51,12 @@ def _ordered(flags: np.ndarray):
 
 
 def build_block_mask(mask: MaskMod, L: int, S: int, q_block: int, kv_block: int, *,
-                     B: int = 1, H: int = 1, q_offset: int = 0) -> dict:
+                     B: int = 1, H: int = 1, q_offset=0, kv_len=None) -> dict:
     """The four BlockMask arrays for a (B, H) grid of masks (1 = broadcast).
+
+    ``q_offset`` and ``kv_len`` may be per-batch sequences (length B); keys at
+    or past kv_len[b] are not visible (a cache of capacity S filled to
+    kv_len[b], charlestar blog, decode section).
 
     Returns int32 arrays ``kv_num_blocks`` (B, H, nQB), ``kv_indices`` (B, H, nQB, nKB),
     ``full_kv_num_blocks``, ``full_kv_indices`` plus the per-tile cell counts.
@@ -67,7 +71,9 @@ def build_block_mask(mask: MaskMod, L: int, S: int, q_block: int, kv_block: int,
     for b in range(B):
         for h in range(H):
             for qb in range(nQB):
-                vis = visible_cells(mask, b, h, L, S, q_offset, qb * q_block, q_block, 0, nKB * kv_block)
+                off = q_offset if np.isscalar(q_offset) else int(q_offset[b])
+                S_b = S if kv_len is None else min(S, int(kv_len if np.isscalar(kv_len) else kv_len[b]))
+                vis = visible_cells(mask, b, h, L, S_b, off, qb * q_block, q_block, 0, nKB * kv_block)
                 cnt = vis.reshape(q_block, nKB, kv_block).sum(axis=(0, 2))
                 counts[b, h, qb] = cnt
                 full = cnt == cells_per_tile
