@@ -148,7 +148,17 @@ typedef enum {
  *   doc_len   must then cover every key and query position, i.e.
  *             doc_len >= max(S, q_offset + L) with q_offset >= 0
  *   n_clauses, clause   PROGRAM: 1 <= n_clauses <= FLEX_MAX_CLAUSES clauses,
- *             all of which must hold */
+ *             all of which must hold
+ *   q_offsets optional device int32[B]: the logical position of query row 0
+ *             per batch, in place of q_offset (values clamped to
+ *             [-2^30, 2^30]); a position outside doc_id has no document
+ *   kv_lens   optional device int32[B]: the valid keys per batch, positions
+ *             [0, kv_lens[b]) of a cache of capacity S (values clamped to
+ *             [0, S]); keys at or past it are hidden whatever the mask says
+ *             (charlestar blog, decode section: capacity is not the filled
+ *             length)
+ *   Either array makes the mask differ between batches: its BlockMask must
+ *   then have B equal to the batch count (build it with B rows). */
 typedef struct {
     int32_t kind;
     int32_t window;
@@ -159,6 +169,8 @@ typedef struct {
     int64_t doc_len;
     int32_t n_clauses;
     flex_mask_clause clause[FLEX_MAX_CLAUSES];
+    const int32_t* q_offsets;
+    const int32_t* kv_lens;
 } flex_mask_params;
 
 /* Score parameters (host struct).  cap > 0 for the SOFTCAP kinds; alibi_m
@@ -364,7 +376,8 @@ size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32
  *                (-inf rows, which saw no key, receive zero gradients)
  *   bm, bmq      the BlockMask of that call and its Q-side lists
  *                (flex_blockmask_transpose); q_block 64 or 128, kv_block a
- *                multiple of 64
+ *                multiple of 64; contiguous caches only, and no per-batch
+ *                q_offsets / kv_lens (UNSUPPORTED)
  *   dq           device (B,Hq,L,D) contiguous, dtype `dtype`
  *   dk, dv       device (B,Hkv,S,D) contiguous, dtype `dtype`
  *   workspace    device scratch of at least flex_attn_bwd_workspace_bytes(),
@@ -381,6 +394,41 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
                           const int64_t v_strides[3], float scale, const flex_score_params* score,
                           const flex_mask_params* mask, const flex_block_mask* bm, const flex_block_mask_q* bmq,
                           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* A paged K/V cache (charlestar blog, decode section: paged or circular
+ * layouts store keys away from their logical positions, and those positions,
+ * not the storage ones, are what masks and distance biases see).  K and V are
+ * pools of num_pages pages of shape (Hkv, page_size, D); logical key j of
+ * batch b lives in row j % page_size of page page_table[b][j / page_size].
+ * A circular (rolling) buffer is the page table p -> p mod (pages in the
+ * ring), with a mask that hides the positions the ring has overwritten.
+ *   page_table  device int32 [B][max_pages]; entries outside [0, num_pages)
+ *               are clamped (the row then reads another page, never past the
+ *               pool)
+ *   page_size   keys per page: a power of two, at least 64
+ *   max_pages   entries per row, max_pages * page_size >= S
+ *   num_pages   pages in each pool */
+typedef struct {
+    const int32_t* page_table;
+    int32_t page_size;
+    int32_t max_pages;
+    int32_t num_pages;
+    int32_t reserved;
+} flex_kv_pages;
+
+/* flex_attn_fwd_aux over a paged K/V cache.  k and v point at the pools;
+ * k_strides and v_strides are {page, head, row} element strides of the pools;
+ * S is the logical capacity of every batch's cache (with kv_lens giving the
+ * filled length per batch).  Every other argument is as for flex_attn_fwd_aux.
+ * Errors: as flex_attn_fwd_aux, plus NULL (pages, page_table), PARAM (page
+ * geometry). */
+flex_status flex_attn_fwd_paged(const void* q, const void* k, const void* v, int32_t dtype,
+                                int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D,
+                                const int64_t q_strides[3], const int64_t k_strides[3],
+                                const int64_t v_strides[3], float scale,
+                                const flex_score_params* score, const flex_mask_params* mask,
+                                const flex_block_mask* bm, const flex_kv_pages* pages, void* out, float* lse,
+                                float* max_scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* flex_status_string(int32_t status);

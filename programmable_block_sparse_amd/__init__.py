@@ -8,6 +8,7 @@ the same names:
   flex_blockmask_build(mask, L, S, q_block, kv_block, ...) -> BlockMask
   flex_attn_fwd(q, k, v, score=..., mask=..., block_mask=..., ...) -> (out, lse)
   flex_attn_fwd_aux(q, k, v, ...) -> (out, lse, max_scores)
+  flex_attn_fwd_paged(q, k_pool, v_pool, page_table, S=..., ...) -> (out, lse, max_scores)
   flex_attn_fwd_workspace_bytes(...)
   flex_blockmask_transpose(block_mask) -> BlockMaskQ
   flex_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
@@ -33,6 +34,7 @@ __all__ = [
     "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
     "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_aux", "flex_attn_fwd_workspace_bytes",
     "BlockMaskQ", "flex_blockmask_transpose", "flex_attn_bwd", "flex_attn_bwd_workspace_bytes",
+    "flex_attn_fwd_paged",
     "flex_status_string", "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "PREDICATES", "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +46,7 @@ MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
                     "flex_blockmask_transpose", "flex_attn_bwd_workspace_bytes", "flex_attn_bwd",
+                    "flex_attn_fwd_paged",
                     "flex_blockmask_to_dense", "flex_blockmask_grid", "flex_blockmask_sparsity",
                     "flex_blockmask_slice", "flex_blockmask_adjust",
                     "flex_status_string", "flex_last_error")
@@ -61,7 +64,8 @@ class flex_mask_params(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32), ("sinks", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("q_offset", ctypes.c_int64), ("doc_id", ctypes.c_void_p),
                 ("doc_len", ctypes.c_int64), ("n_clauses", ctypes.c_int32),
-                ("clause", flex_mask_clause * MAX_CLAUSES)]
+                ("clause", flex_mask_clause * MAX_CLAUSES), ("q_offsets", ctypes.c_void_p),
+                ("kv_lens", ctypes.c_void_p)]
 
 
 class flex_score_params(ctypes.Structure):
@@ -73,6 +77,11 @@ class flex_block_mask(ctypes.Structure):
                 ("kv_block", ctypes.c_int32), ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
                 ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
                 ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+
+
+class flex_kv_pages(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class flex_block_mask_q(ctypes.Structure):
@@ -114,6 +123,11 @@ def load_library():
                                       ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask), P, P, P,
                                       P, ctypes.c_size_t, P]
     lib.flex_attn_fwd_aux.restype = ctypes.c_int
+    lib.flex_attn_fwd_paged.argtypes = [P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3,
+                                        ctypes.c_float, ctypes.POINTER(flex_score_params),
+                                        ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask),
+                                        ctypes.POINTER(flex_kv_pages), P, P, P, P, ctypes.c_size_t, P]
+    lib.flex_attn_fwd_paged.restype = ctypes.c_int
     lib.flex_blockmask_transpose.argtypes = [ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P]
     lib.flex_blockmask_transpose.restype = ctypes.c_int
     lib.flex_attn_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I64, I64, I32, ctypes.POINTER(flex_block_mask)]
@@ -172,11 +186,15 @@ class MaskSpec:
     q_offset: Optional[int] = None
     doc_id: Optional[torch.Tensor] = None   # int32 device tensor for "doc_causal" / the "doc" predicate
     clauses: tuple = ()
+    q_offsets: Optional[torch.Tensor] = None  # int32 device (B,): per-batch logical position of query row 0
+    kv_lens: Optional[torch.Tensor] = None    # int32 device (B,): per-batch filled length of the cache
 
     def to_c(self, L: int, S: int) -> flex_mask_params:
+        ptr = lambda t: None if t is None else t.data_ptr()
         key = (L, S, self.kind, self.window, self.sinks, self.q_offset,
                None if self.doc_id is None else (self.doc_id.data_ptr(), self.doc_id.numel()),
-               tuple(tuple((str(n), int(a)) for n, a in c) for c in self.clauses))
+               tuple(tuple((str(n), int(a)) for n, a in c) for c in self.clauses),
+               ptr(self.q_offsets), ptr(self.kv_lens))
         cached = self.__dict__.get("_c")
         if cached is not None and cached[0] == key:
             return cached[1]
@@ -190,7 +208,12 @@ class MaskSpec:
                 raise ValueError("doc_id must be a contiguous int32 tensor")
             m.doc_id = self.doc_id.data_ptr()
             m.doc_len = self.doc_id.numel()
-        clauses = key[-1]
+        for t in (self.q_offsets, self.kv_lens):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError("q_offsets and kv_lens must be contiguous int32 tensors")
+        m.q_offsets = ptr(self.q_offsets)
+        m.kv_lens = ptr(self.kv_lens)
+        clauses = key[-3]
         if len(clauses) > MAX_CLAUSES or any(len(c) > MAX_LITERALS for c in clauses):
             raise ValueError(f"at most {MAX_CLAUSES} clauses of at most {MAX_LITERALS} predicates")
         m.n_clauses = len(clauses)
@@ -564,6 +587,58 @@ def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
                              dv.data_ptr(), workspace.data_ptr(), ws_bytes,
                              ctypes.c_void_p(_stream_ptr(q.device))))
     return dq, dk, dv
+
+
+def flex_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor, *,
+                        S: int, block_mask: BlockMask, score: Optional[ScoreSpec] = None,
+                        mask: Optional[MaskSpec] = None, scale: Optional[float] = None, return_lse: bool = True,
+                        return_max_scores: bool = False, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, max_scores: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Forward over a paged K/V cache (C: flex_attn_fwd_paged).
+
+    k_pool, v_pool: (num_pages, Hkv, page_size, D) device tensors, last dim
+    contiguous; page_table: int32 (B, max_pages) device tensor; S: the logical
+    capacity per batch.  Returns (out, lse, max_scores) as flex_attn_fwd_aux."""
+    lib = load_library()
+    score = score or ScoreSpec()
+    mask = mask or MaskSpec()
+    B, Hq, L, D = q.shape
+    num_pages, Hkv, page_size = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if v_pool.shape != k_pool.shape or k_pool.shape[3] != D:
+        raise ValueError(f"pool shapes {tuple(k_pool.shape)} / {tuple(v_pool.shape)} do not match q {tuple(q.shape)}")
+    if not (q.dtype == k_pool.dtype == v_pool.dtype) or q.dtype not in DTYPES:
+        raise ValueError("q and the pools must share a dtype, float32 or bfloat16")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.dim() != 2 \
+            or page_table.shape[0] != B:
+        raise ValueError("page_table must be a contiguous int32 (B, max_pages) tensor")
+    for t in (q, k_pool, v_pool):
+        if t.stride(3) != 1:
+            raise ValueError("the last dimension must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
+    lse = (lse if lse is not None else torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)) \
+        if return_lse else None
+    max_scores = (max_scores if max_scores is not None else
+                  torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)) if return_max_scores else None
+    cbm = block_mask.to_c()
+    ws_bytes = int(lib.flex_attn_fwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    pages = flex_kv_pages()
+    pages.page_table = page_table.data_ptr()
+    pages.page_size, pages.max_pages, pages.num_pages = page_size, page_table.shape[1], num_pages
+    st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    cs, cm = score.to_c(), mask.to_c(L, S)
+    _check(lib.flex_attn_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv,
+                                   L, S, D, st(q), st(k_pool), st(v_pool),
+                                   ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs),
+                                   ctypes.byref(cm), ctypes.byref(cbm), ctypes.byref(pages), out.data_ptr(),
+                                   None if lse is None else lse.data_ptr(),
+                                   None if max_scores is None else max_scores.data_ptr(),
+                                   None if not ws_bytes else workspace.data_ptr(), ws_bytes,
+                                   ctypes.c_void_p(_stream_ptr(q.device))))
+    return out, lse, max_scores
 
 
 def default_scale(D: int) -> float:

@@ -231,16 +231,45 @@ __device__ __forceinline__ StageOffsets<T, D> stage_offsets(int64_t k_sr, int64_
     return so;
 }
 
+// Where the K and V rows of the tile starting at logical key kv0 live: buffer
+// descriptors and byte offsets.  A contiguous cache uses the head slice's
+// descriptors.  A paged cache (PAGED kernels only) sends the logical page
+// kv0 >> page_shift through the batch's page-table row to a physical page of
+// the pool; masks and biases keep using the logical position kv0.
+struct TileAddr {
+    __amdgpu_buffer_rsrc_t k, v;
+    int ko, vo;
+};
+
+template <typename T, bool PAGED>
+__device__ __forceinline__ TileAddr tile_addr(const FwdArgs& a, const SliceRsrc& sr, const T* kbase, const T* vbase,
+                                              int b, int kv0) {
+    TileAddr t{sr.k, sr.v, kv0 * sr.k_row_bytes, kv0 * sr.v_row_bytes};
+    if constexpr (PAGED) {
+        if (a.page_table != nullptr) {
+            const int lp = kv0 >> a.page_shift;
+            int page = scalar_load(a.page_table + (int64_t)b * a.max_pages + lp);
+            page = min(max(page, 0), a.num_pages - 1);       // a bad entry reads another page, never outside the pool
+            const int in_page = kv0 - (lp << a.page_shift);
+            const int page_rows = 1 << a.page_shift;
+            t.k = slice_rsrc(kbase + (int64_t)page * a.k_sb, sr.k_row_bytes, page_rows);
+            t.v = slice_rsrc(vbase + (int64_t)page * a.v_sb, sr.v_row_bytes, page_rows);
+            t.ko = in_page * sr.k_row_bytes;
+            t.vo = in_page * sr.v_row_bytes;
+        }
+    }
+    return t;
+}
+
 template <typename T, int D>
-__device__ __forceinline__ void stage_load(Stage<T, D>& st, const StageOffsets<T, D>& so, const SliceRsrc& sr, int kv0,
-                                           bool with_doc, int tid) {
-    const int ko = kv0 * sr.k_row_bytes, vo = kv0 * sr.v_row_bytes;
+__device__ __forceinline__ void stage_load(Stage<T, D>& st, const StageOffsets<T, D>& so, const TileAddr& ta,
+                                           const SliceRsrc& sr, int kv0, bool with_doc, int tid) {
 #pragma unroll
     for (int u = 0; u < Stage<T, D>::kKUnits; ++u)
-        st.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.k, so.k[u], ko, 0));
+        st.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ta.k, so.k[u], ta.ko, 0));
 #pragma unroll
     for (int u = 0; u < Stage<T, D>::kVUnits; ++u)
-        st.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.v, so.v[u], vo, 0));
+        st.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ta.v, so.v[u], ta.vo, 0));
     if (with_doc && tid < kTileN) st.doc = __builtin_amdgcn_raw_buffer_load_b32(sr.doc, tid * 4, kv0 * 4, 0);
 }
 
@@ -760,13 +789,13 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // plus an immediate.  Per tile: wait for this wave's part of the tile, barrier
 // (publishes the tile and frees the buffer computed last), refill that buffer
 // with the tile STAGES - 1 ahead, compute.
-template <int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES>
+template <int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES, bool PAGED>
 __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* __restrict__ kbase,
                                                 const __bf16* __restrict__ vbase, const QRegs<__bf16, D>& qr,
                                                 const int* __restrict__ part_idx, int n_part,
                                                 const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                                 const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
-                                                f32x16_t (&o)[D / 32], RowState<false>& st, char* lds) {
+                                                f32x16_t (&o)[D / 32], RowState<false>& st, char* lds, int S, int b) {
     using G = Tiles<__bf16, D>;
     static_assert(STAGES >= 2, "at least double buffering");
     const int tid = threadIdx.x;
@@ -787,8 +816,8 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     SliceRsrc sr;
     sr.k_row_bytes = (int)(a.k_sr * (int64_t)sizeof(__bf16));
     sr.v_row_bytes = (int)(a.v_sr * (int64_t)sizeof(__bf16));
-    sr.k = slice_rsrc(kbase, sr.k_row_bytes, a.S);
-    sr.v = slice_rsrc(vbase, sr.v_row_bytes, a.S);
+    sr.k = slice_rsrc(kbase, sr.k_row_bytes, S);
+    sr.v = slice_rsrc(vbase, sr.v_row_bytes, S);
     sr.doc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
     const DmaPlan<D> pl = dma_plan<D>(sr.k_row_bytes, sr.v_row_bytes, wave, lane);
     // key-split waves read only their own key half: fold it into the offsets
@@ -797,15 +826,15 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     // K and V instructions per wave and tile (wave 0 adds one doc-id load).
     constexpr int kPerTile = 2 * DmaPlan<D>::kInsts;
     auto issue = [&](char* buf, int kv0) {
-        const int ko = kv0 * sr.k_row_bytes, vo = kv0 * sr.v_row_bytes;
+        const TileAddr ta = tile_addr<__bf16, PAGED>(a, sr, kbase, vbase, b, kv0);
 #pragma unroll
         for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.k, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
-                                                     ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ta.k, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
+                                                     ta.ko, 0, 0);
 #pragma unroll
         for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr.v, (lds_void_t*)(buf + G::kElemsK * 2 + (i * 4 + wave) * 1024),
-                                                     16, pl.v[i], vo, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ta.v, (lds_void_t*)(buf + G::kElemsK * 2 + (i * 4 + wave) * 1024),
+                                                     16, pl.v[i], ta.vo, 0, 0);
         if (with_doc && wave == 0) {
             // lane id from mbcnt: cheap to recompute, so it is not kept live
             const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
@@ -845,11 +874,11 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
         const bool masked = ring_masked[B];
         if (wave_active) {
             if constexpr (KSPLIT) {
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, kh, 0,
+                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, kh, 0,
                                                       lane);
             } else {
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 0, 0, lane);
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 1, 1, lane);
+                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 0, 0, lane);
+                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 1, 1, lane);
             }
         }
     };
@@ -866,15 +895,16 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
 // Walk tiles [tile_lo, tile_hi) of one row block's lists: partial tiles (masked)
 // first, then full tiles.  All waves load; active waves compute either key half
 // kh of every tile (KSPLIT) or both halves.
-template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES = 2>
+template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES = 2, bool PAGED = false>
 __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restrict__ kbase, const T* __restrict__ vbase,
                                             const QRegs<T, D>& qr, const int* __restrict__ part_idx, int n_part,
                                             const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                             const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
-                                            f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds) {
+                                            f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds, int S,
+                                            int b) {
     if constexpr (sizeof(T) == 2) {
-        attend_rows_dma<D, SCORE, FIXED, KSPLIT, EXT, STAGES>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
-                                                         tile_hi, tc, row, wave_active, kh, o, st, lds);
+        attend_rows_dma<D, SCORE, FIXED, KSPLIT, EXT, STAGES, PAGED>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
+                                                         tile_hi, tc, row, wave_active, kh, o, st, lds, S, b);
     } else {
     using G = Tiles<T, D>;
     const LdsAddr<T, D> la{};
@@ -897,13 +927,13 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
     SliceRsrc sr;
     sr.k_row_bytes = (int)(a.k_sr * (int64_t)sizeof(T));
     sr.v_row_bytes = (int)(a.v_sr * (int64_t)sizeof(T));
-    sr.k = slice_rsrc(kbase, sr.k_row_bytes, a.S);
-    sr.v = slice_rsrc(vbase, sr.v_row_bytes, a.S);
+    sr.k = slice_rsrc(kbase, sr.k_row_bytes, S);
+    sr.v = slice_rsrc(vbase, sr.v_row_bytes, S);
     sr.doc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
     Stage<T, D> stage;
     bool masked;
     int kv0 = tile_kv0(tile_lo, masked);
-    stage_load<T, D>(stage, so, sr, kv0, with_doc, tid);
+    stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, kv0), sr, kv0, with_doc, tid);
     stage_store<T, D>(stage, lds, with_doc, tid);
     __syncthreads();
     for (int t = tile_lo; t < tile_hi; ++t) {
@@ -913,15 +943,16 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
         const bool has_next = t + 1 < tile_hi;
         if (has_next) {
             next_kv0 = tile_kv0(t + 1, next_masked);
-            stage_load<T, D>(stage, so, sr, next_kv0, with_doc, tid);
+            stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, next_kv0), sr, next_kv0, with_doc,
+                             tid);
         }
         const char* cur = lds + buf * G::kBufBytes;
         if (wave_active) {
             if constexpr (KSPLIT) {
-                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, kh, kh, lane);
+                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, kh, kh, lane);
             } else {
-                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 0, 0, lane);
-                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, a.S, row, 1, 1, lane);
+                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 0, 0, lane);
+                process_tile<T, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 1, 1, lane);
             }
         }
         if (has_next) stage_store<T, D>(stage, lds + (buf ^ 1) * G::kBufBytes, with_doc, tid);
@@ -1011,6 +1042,33 @@ __device__ __forceinline__ int lane_doc(const MaskArgs& m, int q_pos) {
 // workgroups at head dim 64 (the score pipeline is VALU-bound there, so more
 // waves hide MFMA and LDS latency behind each other's VALU work), otherwise
 // as many as the registers of the wider tiles allow.
+// Per-batch view of the call (paged / per-batch kernels only): the logical position of
+// query row 0 and the number of valid keys of batch b, when the mask carries
+// per-batch arrays (values clamped into range), and the K/V base of the head
+// (a paged pool has no batch term: pages carry it).
+struct BatchView {
+    int q_offset;
+    int S;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ BatchView batch_view(const FwdArgs& a, int b) {
+    BatchView v{a.mask.q_offset, a.S};
+    if constexpr (PAGED) {
+        if (a.mask.q_offsets != nullptr)
+            v.q_offset = min(max(scalar_load(a.mask.q_offsets + b), -(1 << 30)), 1 << 30);
+        if (a.mask.kv_lens != nullptr) v.S = min(max(scalar_load(a.mask.kv_lens + b), 0), a.S);
+    }
+    return v;
+}
+
+template <typename T, bool PAGED>
+__device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, int64_t sh, const FwdArgs& a, int b,
+                                                 int hkv) {
+    const int64_t off = (PAGED && a.page_table != nullptr) ? (int64_t)hkv * sh : (int64_t)b * sb + (int64_t)hkv * sh;
+    return reinterpret_cast<const T*>(base) + off;
+}
+
 template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
     static constexpr int value =
         sizeof(T) == 2 ? (D == 64 ? ((KSPLIT && !EXT) ? 4 : 3) : 2) : (D == 64 ? 2 : 1);
@@ -1024,7 +1082,7 @@ template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
 // rows) and key half w >> 1 of every tile, which halves the tile loop of a
 // workgroup (short critical path when a few Q blocks hold most of the work);
 // otherwise a part is 128 rows, one 32-row group per wave, both key halves.
-template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT>
+template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, bool PAGED>
 __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT>::value)) void attn_fwd_prefill(FwdArgs a) {
     using G = Tiles<T, D>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::kBufBytes];
@@ -1051,14 +1109,15 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT>::val
     LaneRow row;
     row.q_row = qb * a.q_block + r_in_blk;
     row.ok = r_in_blk < a.q_block && row.q_row < a.L;
-    row.q_pos = row.q_row + a.mask.q_offset;
+    const BatchView bv = batch_view<PAGED>(a, b);
+    row.q_pos = row.q_row + bv.q_offset;
     row.hq = hq;
     row.doc_q = lane_doc(a.mask, row.q_pos);
     const bool wave_active = part * kRows + rg * 32 < a.q_block;
 
     const T* qbase = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
-    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const T* kbase = kv_head_base<T, PAGED>(a.k, a.k_sb, a.k_sh, a, b, hkv);
+    const T* vbase = kv_head_base<T, PAGED>(a.v, a.v_sb, a.v_sh, a, b, hkv);
 
     QRegs<T, D> qr;
     load_q<T, D>(qr, qbase + (int64_t)row.q_row * a.q_sr, row.ok, hf);
@@ -1074,9 +1133,9 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT>::val
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     RowState<Precise<T>::value> st{kNegInf, 0.0f, 0.0f, kNegInf};
-    attend_rows<T, D, SCORE, FIXED, KSPLIT, EXT>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB, n_part,
+    attend_rows<T, D, SCORE, FIXED, KSPLIT, EXT, 2, PAGED>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB, n_part,
                                             a.full_idx + row_id * a.nKB, 0, n_tiles, tc, row, wave_active, kh, o, st,
-                                            lds);
+                                            lds, bv.S, b);
     if constexpr (KSPLIT) merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
 
     // Epilogue: out = acc / lr (0 for rows that saw no key), lse = ln(sum).
@@ -1128,7 +1187,7 @@ template <int D> struct DecodeShape {
 // divided into `splits` contiguous ranges; each workgroup writes its partial
 // numerator, base-2 reference and denominator.  bf16 only; the block mask must
 // be the same for every head (H = 1).
-template <int D, int SCORE, bool FIXED, bool EXT>
+template <int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
 __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_fwd_decode(FwdArgs a) {
     using T = __bf16;
     using G = Tiles<T, D>;
@@ -1148,14 +1207,15 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
     row.q_row = qb * a.q_block + r % a.q_block;
     row.hq = hkv * a.group + g;
     row.ok = r < rows && row.q_row < a.L;
-    row.q_pos = row.q_row + a.mask.q_offset;
+    const BatchView bv = batch_view<PAGED>(a, b);
+    row.q_pos = row.q_row + bv.q_offset;
     row.doc_q = lane_doc(a.mask, row.q_pos);
     const bool wave_active = rg * 32 < rows;
 
     const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)row.hq * a.q_sh +
                     (int64_t)row.q_row * a.q_sr;
-    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const T* kbase = kv_head_base<T, PAGED>(a.k, a.k_sb, a.k_sh, a, b, hkv);
+    const T* vbase = kv_head_base<T, PAGED>(a.v, a.v_sb, a.v_sh, a, b, hkv);
     QRegs<T, D> qr;
     load_q<T, D>(qr, qrow, row.ok, hf);
 
@@ -1172,9 +1232,9 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     RowState<false> st{kNegInf, 0.0f, 0.0f, kNegInf};
-    attend_rows<T, D, SCORE, FIXED, true, EXT, DecodeShape<D>::kStages>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
+    attend_rows<T, D, SCORE, FIXED, true, EXT, DecodeShape<D>::kStages, PAGED>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
                                                                    n_part, a.full_idx + row_id * a.nKB, t_lo, t_hi,
-                                                                   tc, row, wave_active, kh, o, st, lds);
+                                                                   tc, row, wave_active, kh, o, st, lds, bv.S, b);
     merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
 
     const float l = wave_half_sum(st.l);
@@ -1238,30 +1298,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_combine(FwdArgs a) {
         a.lse[row] = live ? (float)(((double)ref_max + (double)__log2f(l)) * 0.6931471805599453) : kNegInf;
 }
 
-template <typename T, int D, int SCORE, bool FIXED, bool EXT>
+template <typename T, int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const int rows = a.ksplit ? 64 : 128;
     const int64_t blocks = (int64_t)a.nQB * ((a.q_block + rows - 1) / rows) * a.B * a.Hq;
     if constexpr (D == 64) {
         // head dim 64 always uses key-split workgroups (prefill_ksplit)
         if (!a.ksplit) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT>), dim3((unsigned)blocks), dim3(kThreads), 0,
+        hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, a);
     } else {
         if (a.ksplit)
-            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, PAGED>), dim3((unsigned)blocks),
                                dim3(kThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, false, EXT>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, false, EXT, PAGED>), dim3((unsigned)blocks),
                                dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
 
-template <int D, int SCORE, bool FIXED, bool EXT>
+template <int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
 hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.B * a.Hkv * a.nQB * a.splits;
-    hipLaunchKernelGGL((attn_fwd_decode<D, SCORE, FIXED, EXT>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_decode<D, SCORE, FIXED, EXT, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)a.B * a.Hq * a.L;
@@ -1270,44 +1330,48 @@ hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DECODE, bool EXT>
+template <typename T, int D, bool DECODE, bool EXT, bool PAGED>
 hipError_t dispatch_ext(const FwdArgs& a, hipStream_t stream) {
     const bool fixed = a.ref_mode == 1;
     if constexpr (DECODE) {
         switch (a.score_kind) {
-        case SCORE_NONE: return launch_decode<D, SCORE_NONE, false, EXT>(a, stream);
+        case SCORE_NONE: return launch_decode<D, SCORE_NONE, false, EXT, PAGED>(a, stream);
         case SCORE_SOFTCAP:
-            return fixed ? launch_decode<D, SCORE_SOFTCAP, true, EXT>(a, stream)
-                         : launch_decode<D, SCORE_SOFTCAP, false, EXT>(a, stream);
+            return fixed ? launch_decode<D, SCORE_SOFTCAP, true, EXT, PAGED>(a, stream)
+                         : launch_decode<D, SCORE_SOFTCAP, false, EXT, PAGED>(a, stream);
         case SCORE_SOFTCAP_ALIBI:
-            return fixed ? launch_decode<D, SCORE_SOFTCAP_ALIBI, true, EXT>(a, stream)
-                         : launch_decode<D, SCORE_SOFTCAP_ALIBI, false, EXT>(a, stream);
-        case SCORE_ALIBI: return launch_decode<D, SCORE_ALIBI, false, EXT>(a, stream);
+            return fixed ? launch_decode<D, SCORE_SOFTCAP_ALIBI, true, EXT, PAGED>(a, stream)
+                         : launch_decode<D, SCORE_SOFTCAP_ALIBI, false, EXT, PAGED>(a, stream);
+        case SCORE_ALIBI: return launch_decode<D, SCORE_ALIBI, false, EXT, PAGED>(a, stream);
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (a.score_kind) {
-        case SCORE_NONE: return launch_prefill<T, D, SCORE_NONE, false, EXT>(a, stream);
+        case SCORE_NONE: return launch_prefill<T, D, SCORE_NONE, false, EXT, PAGED>(a, stream);
         case SCORE_SOFTCAP:
             if constexpr (sizeof(T) == 2)
-                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP, true, EXT>(a, stream);
-            return launch_prefill<T, D, SCORE_SOFTCAP, false, EXT>(a, stream);
+                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP, true, EXT, PAGED>(a, stream);
+            return launch_prefill<T, D, SCORE_SOFTCAP, false, EXT, PAGED>(a, stream);
         case SCORE_SOFTCAP_ALIBI:
             if constexpr (sizeof(T) == 2)
-                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, true, EXT>(a, stream);
-            return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, false, EXT>(a, stream);
-        case SCORE_ALIBI: return launch_prefill<T, D, SCORE_ALIBI, false, EXT>(a, stream);
+                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, true, EXT, PAGED>(a, stream);
+            return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, false, EXT, PAGED>(a, stream);
+        case SCORE_ALIBI: return launch_prefill<T, D, SCORE_ALIBI, false, EXT, PAGED>(a, stream);
         default: return hipErrorInvalidValue;
         }
     }
 }
 
 // Program masks and the max_scores output run in separately compiled
-// "extended" kernels, so the common kernels keep their register budget.
+// "extended" kernels, so the common kernels keep their register budget; paged
+// caches and per-batch offsets and lengths in a third set (extended kernels
+// that also remap tiles and read per-batch values).
 template <typename T, int D, bool DECODE>
 hipError_t dispatch(const FwdArgs& a, hipStream_t stream) {
-    if (a.mask.kind == MASK_PROGRAM || a.max_scores != nullptr) return dispatch_ext<T, D, DECODE, true>(a, stream);
-    return dispatch_ext<T, D, DECODE, false>(a, stream);
+    if (a.page_table != nullptr || a.mask.q_offsets != nullptr || a.mask.kv_lens != nullptr)
+        return dispatch_ext<T, D, DECODE, true, true>(a, stream);
+    if (a.mask.kind == MASK_PROGRAM || a.max_scores != nullptr) return dispatch_ext<T, D, DECODE, true, false>(a, stream);
+    return dispatch_ext<T, D, DECODE, false, false>(a, stream);
 }
 
 }  // namespace

@@ -271,9 +271,13 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
     const int row0 = qb * a.q_block;
     const int rows = min(a.q_block, a.L - row0);
     const int64_t row_id = (int64_t)bh * a.nQB + qb;
-    const int p0 = row0 + a.mask.q_offset, p1 = p0 + rows - 1;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int h = bh % a.Hm;   // query head of this mask row (0 when broadcast)
+    const int bb = bh / a.Hm;  // batch of this mask row
+    // per-batch logical offset of row 0 and valid key count (clamped into range)
+    const int q_offset = a.mask.q_offsets ? min(max(a.mask.q_offsets[bb], -(1 << 30)), 1 << 30) : a.mask.q_offset;
+    const int S = a.mask.kv_lens ? min(max(a.mask.kv_lens[bb], 0), a.S) : a.S;
+    const int p0 = row0 + q_offset, p1 = p0 + rows - 1;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if constexpr (KIND == MASK_PROGRAM) {
         if (!a.mask.uses_doc && threadIdx.x == 0) {
             // one run holding every row, with no document
@@ -315,9 +319,11 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
             const int kb = w * 16 + t;
             if (kb >= a.nKB) break;
             const int c0 = kb * a.kv_block;
-            const int c1 = min(c0 + a.kv_block, a.S) - 1;
-            const bool clipped = rows < a.q_block || c0 + a.kv_block > a.S;
-            word |= (uint32_t)corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped, h) << (2 * t);
+            const int c1 = min(c0 + a.kv_block, S) - 1;
+            const bool clipped = rows < a.q_block || c0 + a.kv_block > S;
+            // tiles past the valid keys are empty
+            const int cls = c0 >= S ? TILE_EMPTY : corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped, h);
+            word |= (uint32_t)cls << (2 * t);
         }
         tile_class[w] = word;
     }
@@ -346,13 +352,13 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
 #pragma unroll
                     for (int u = 0; u < kCountBatch; ++u) {
                         const int col = (kb0 + u * kBuildWaves) * a.kv_block + jj;
-                        doc_col[u] = (todo[u] && jj < a.kv_block && col < a.S) ? doc_at(a.mask, col, -1) : -1;
+                        doc_col[u] = (todo[u] && jj < a.kv_block && col < S) ? doc_at(a.mask, col, -1) : -1;
                     }
                 }
 #pragma unroll
                 for (int u = 0; u < kCountBatch; ++u) {
                     const int col = (kb0 + u * kBuildWaves) * a.kv_block + jj;
-                    if (!todo[u] || jj >= a.kv_block || col >= a.S) continue;
+                    if (!todo[u] || jj >= a.kv_block || col >= S) continue;
                     // rows of this column that pass the causal part: p in [max(p0, col), p1]
                     const int lo = max(p0, col);
                     if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS) {

@@ -54,6 +54,8 @@ struct MaskArgs {
     int doc_len;
     int uses_doc;    // the mask compares document ids (DOC_CAUSAL, or a DOC predicate)
     MaskProgram prog;
+    const int* q_offsets;   // per batch: logical position of query row 0 (NULL: q_offset)
+    const int* kv_lens;     // per batch: valid keys, positions [0, kv_lens[b]) (NULL: S)
 };
 
 // floor(a / b) for b > 0.

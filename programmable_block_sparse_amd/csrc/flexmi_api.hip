@@ -84,9 +84,11 @@ flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
             }
         }
     }
+    if ((reinterpret_cast<uintptr_t>(m->q_offsets) & 3u) || (reinterpret_cast<uintptr_t>(m->kv_lens) & 3u))
+        return fail(FLEX_ERR_LAYOUT, "q_offsets and kv_lens must be 4-byte aligned");
     if (m->kind == FLEX_MASK_DOC_CAUSAL || program_uses(m, FLEX_PRED_DOC)) {
         if (m->doc_id == nullptr) return fail(FLEX_ERR_NULL, "a document mask needs doc_id");
-        if (m->q_offset < 0) return fail(FLEX_ERR_PARAM, "a document mask needs q_offset >= 0");
+        if (m->q_offset < 0 && !m->q_offsets) return fail(FLEX_ERR_PARAM, "a document mask needs q_offset >= 0");
         const int64_t need = std::max<int64_t>(S, m->q_offset + L);
         if (m->doc_len < need || m->doc_len >= kMaxLen)
             return fail(FLEX_ERR_PARAM, "doc_len %lld must cover max(S, q_offset + L) = %lld",
@@ -117,8 +119,12 @@ MaskArgs to_mask_args(const flex_mask_params* m) {
         }
     }
     if (!a.uses_doc) a.doc_len = 0;
+    a.q_offsets = m->q_offsets;
+    a.kv_lens = m->kv_lens;
     return a;
 }
+
+bool per_batch(const flex_mask_params* m) { return m->q_offsets != nullptr || m->kv_lens != nullptr; }
 
 flex_status check_bm_arrays(const flex_block_mask* bm) {
     if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
@@ -283,6 +289,8 @@ static flex_status check_fwd(const void* q, const void* k, const void* v, int32_
     if (flex_status s = check_mask(mask, L, S)) return s;
     if (program_uses(mask, FLEX_PRED_HEAD_LT) && bm->H != Hq)
         return fail(FLEX_ERR_BLOCKMASK, "the mask reads the query head: block mask H=%d must be Hq=%d", bm->H, Hq);
+    if (per_batch(mask) && bm->B != B)
+        return fail(FLEX_ERR_BLOCKMASK, "per-batch offsets or lengths: block mask B=%d must be B=%d", bm->B, B);
     return FLEX_OK;
 }
 
@@ -303,16 +311,32 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
                              bm, out, lse, nullptr, workspace, workspace_bytes, stream);
 }
 
-flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+static flex_status fwd_common(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
                               int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
                               const int64_t k_strides[3], const int64_t v_strides[3], float scale,
                               const flex_score_params* score, const flex_mask_params* mask,
-                              const flex_block_mask* bm, void* out, float* lse, float* max_scores, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-    g_last_error.clear();
+                              const flex_block_mask* bm, const flex_kv_pages* pages, void* out, float* lse,
+                              float* max_scores, void* workspace, size_t workspace_bytes, void* stream) {
     if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
                                   bm, out, lse))
         return s;
+    int page_shift = 0;
+    if (pages) {
+        if (!pages->page_table) return fail(FLEX_ERR_NULL, "page_table must not be NULL");
+        if (reinterpret_cast<uintptr_t>(pages->page_table) & 3u)
+            return fail(FLEX_ERR_LAYOUT, "page_table must be 4-byte aligned");
+        const int32_t ps = pages->page_size;
+        if (ps < 64 || ps > (1 << 20) || (ps & (ps - 1)))
+            return fail(FLEX_ERR_PARAM, "page_size must be a power of two in [64, 2^20] (got %d)", ps);
+        while ((1 << page_shift) < ps) ++page_shift;
+        if (pages->num_pages < 1 || pages->max_pages < 1 || (int64_t)pages->max_pages * ps < S)
+            return fail(FLEX_ERR_PARAM, "max_pages * page_size must cover S and num_pages be >= 1");
+        if ((int64_t)B * pages->max_pages >= (int64_t(1) << 31)) return fail(FLEX_ERR_PARAM, "page table too large");
+        const int64_t elem = dtype == FLEX_BF16 ? 2 : 4;
+        if ((int64_t)ps * std::max(k_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31) ||
+            (int64_t)ps * std::max(v_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31))
+            return fail(FLEX_ERR_UNSUPPORTED, "one page of one head must stay below 2 GiB");
+    }
     if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
     if (max_scores && (reinterpret_cast<uintptr_t>(max_scores) & 3u))
         return fail(FLEX_ERR_LAYOUT, "max_scores must be 4-byte aligned");
@@ -365,12 +389,16 @@ flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32
         const double c2 = (double)score->cap * 1.4426950408889634;
         bool ok = c2 <= 92.0;
         if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI)
-            ok = ok && mask_implies_causal(mask) && mask->q_offset + L <= S;
+            ok = ok && mask_implies_causal(mask) && mask->q_offset + L <= S && !per_batch(mask);
         if (ok) {
             a.ref_mode = 1;
             a.ref_fixed = (float)(c2 <= 63.0 ? c2 : 120.0 - c2);
         }
     }
+    a.page_table = pages ? pages->page_table : nullptr;
+    a.page_shift = page_shift;
+    a.max_pages = pages ? pages->max_pages : 0;
+    a.num_pages = pages ? pages->num_pages : 0;
     a.ksplit = prefill_ksplit(dtype, B, Hq, bm->num_q_blocks, bm->q_block, D);
     a.splits = decode_splits(dtype, B, Hq, Hkv, (int)L, D, bm->q_block, bm->kv_block, bm->num_kv_blocks, bm->H);
     a.ws_acc = nullptr;
@@ -384,6 +412,29 @@ flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32
     hipError_t e = launch_attn_fwd(dtype, D, a, as_stream(stream));
     if (e != hipSuccess) return fail(FLEX_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return FLEX_OK;
+}
+
+flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                              int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                              const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                              const flex_score_params* score, const flex_mask_params* mask,
+                              const flex_block_mask* bm, void* out, float* lse, float* max_scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    return fwd_common(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, scale, score, mask, bm,
+                      nullptr, out, lse, max_scores, workspace, workspace_bytes, stream);
+}
+
+flex_status flex_attn_fwd_paged(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                                int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                                const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                                const flex_score_params* score, const flex_mask_params* mask,
+                                const flex_block_mask* bm, const flex_kv_pages* pages, void* out, float* lse,
+                                float* max_scores, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!pages) return fail(FLEX_ERR_NULL, "pages must not be NULL");
+    return fwd_common(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, scale, score, mask, bm,
+                      pages, out, lse, max_scores, workspace, workspace_bytes, stream);
 }
 
 flex_status flex_blockmask_transpose(const flex_block_mask* bm, const flex_block_mask_q* bmq, void* stream) {
@@ -447,6 +498,8 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
         return fail(FLEX_ERR_BLOCKMASK, "Q-side block mask dims differ from the block mask's");
     if (bm->q_block != 64 && bm->q_block != 128)
         return fail(FLEX_ERR_UNSUPPORTED, "the backward pass needs q_block 64 or 128 (got %d)", bm->q_block);
+    if (per_batch(mask))
+        return fail(FLEX_ERR_UNSUPPORTED, "the backward pass takes no per-batch q_offsets / kv_lens");
     if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return fail(FLEX_ERR_LAYOUT, "dout, dq, dk and dv must be 16-byte aligned");

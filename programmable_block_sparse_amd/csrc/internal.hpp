@@ -108,6 +108,13 @@ struct FwdArgs {
     float ref_fixed;
     // prefill row layout: 1 = 64-row workgroups, key halves split across waves
     int ksplit;
+    // paged K/V pool (page_table == NULL: contiguous (B, Hkv, S, D) caches):
+    // k, v point at pools of num_pages pages, k_sb / v_sb the page strides;
+    // page_table[b][p] is the physical page of logical page p of batch b
+    const int* page_table;
+    int page_shift;     // log2(page size); a power of two >= 64
+    int max_pages;
+    int num_pages;
     // split-KV decode (splits == 0: prefill kernel)
     float* ws_acc;      // [splits][B][Hq][L][D] partial numerators
     float* ws_ml;       // [splits][B][Hq][L][4]  partial (base-2 reference, sum p, sum rounded p, max score)

@@ -370,3 +370,40 @@ def test_blockmask_utilities_reject(lib):
     assert lib.flex_blockmask_adjust(ref(bm), 200, 400, ref(_bm(200, 400, 128, 64, B=2, H=3)), None) == BLOCKMASK
     assert lib.flex_blockmask_adjust(ref(bm), 0, 100, ref(adj), None) == SHAPE
     assert lib.flex_blockmask_adjust(ref(bm), 200, 100, ref(_bm(200, 100, 128, 64)), None) == BLOCKMASK
+
+
+def test_paged_forward_rejects(lib):
+    f = Fwd(L=16, S=1000, qb=16)
+    a3 = lambda x: (ctypes.c_int64 * 3)(*x)
+    pages = pbs.flex_kv_pages()
+    pages.page_table, pages.page_size, pages.max_pages, pages.num_pages = FAKE, 64, 16, 40
+
+    def call(pg):
+        return lib.flex_attn_fwd_paged(f.q, f.k, f.v, f.dtype, f.B, f.Hq, f.Hkv, f.L, f.S, f.D, a3(f.qs),
+                                       a3([64 * 64 * 2, 64 * 64, 64]), a3([64 * 64 * 2, 64 * 64, 64]),
+                                       ctypes.c_float(0.0), ctypes.byref(f.score), ctypes.byref(f.mask),
+                                       ctypes.byref(f.bm), None if pg is None else ctypes.byref(pg), f.out, f.lse,
+                                       None, None, 0, None)
+    assert call(pages) in (OK, HIP), pbs.flex_last_error()
+    assert call(None) == NULL
+    for field, bad, code in (("page_size", 48, PARAM), ("page_size", 96, PARAM), ("page_size", 32, PARAM),
+                             ("max_pages", 15, PARAM), ("num_pages", 0, PARAM), ("page_table", None, NULL),
+                             ("page_table", FAKE + 2, LAYOUT)):
+        pg = pbs.flex_kv_pages()
+        pg.page_table, pg.page_size, pg.max_pages, pg.num_pages = FAKE, 64, 16, 40
+        setattr(pg, field, bad)
+        assert call(pg) == code, (field, bad, pbs.flex_last_error())
+
+
+def test_per_batch_arrays_need_per_batch_block_mask(lib):
+    f = Fwd()
+    f.mask.kv_lens = FAKE
+    assert f.call(lib) == BLOCKMASK                       # block mask B=1 but two batches
+    f.bm.B = f.B
+    assert f.call(lib) in (OK, HIP)
+    f.mask.q_offsets = FAKE + 2
+    assert f.call(lib) == LAYOUT
+    b = Bwd()
+    b.mask.kv_lens = FAKE
+    b.bm.B = b.bmq.B = b.B
+    assert b.call(lib) == UNSUPPORTED                     # the backward takes none

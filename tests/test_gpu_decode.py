@@ -1,0 +1,115 @@
+"""GPU parity of the decode extensions: per-batch query offsets and filled
+lengths of a cache, paged K/V pools (and a circular buffer expressed as a
+page table), through the C ABI against the CPU oracle on the logical K/V."""
+import numpy as np
+import pytest
+import torch
+
+import programmable_block_sparse_amd as pbs
+from gpu_common import assert_attention_close, assert_block_mask_equal, require_gpu
+from oracle import MaskMod, ScoreMod, attention, build_block_mask
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _t(x, dtype, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(f32_to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+def _w(x, dtype):
+    return bf16_bits_to_f32(f32_to_bf16_bits(x)) if dtype == "bf16" else x
+
+
+def _i32(x, dev):
+    return torch.tensor(np.asarray(x, dtype=np.int32), device=dev)
+
+
+def run(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, kind, window=0, sinks=0, offs, lens,
+        page_size=0, ring_pages=0, what=""):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    spec = pbs.MaskSpec(kind, window=window, sinks=sinks, q_offset=0, q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev))
+    mod = MaskMod(kind, window=window, sinks=sinks)
+    bm = pbs.flex_blockmask_build(spec, L, S, qb, kb, B=B, device=dev)
+    assert_block_mask_equal(bm, build_block_mask(mod, L, S, qb, kb, B=B, q_offset=offs, kv_len=lens))
+    sspec, smod = pbs.ScoreSpec(**score), ScoreMod(**score)
+    qt = _t(q, dtype, dev)
+    if page_size:
+        n_log = -(-S // page_size)
+        if ring_pages:
+            # a rolling buffer: logical page p of every batch in ring slot p mod ring_pages
+            n_phys = B * ring_pages
+            table = np.array([[b * ring_pages + p % ring_pages for p in range(n_log)] for b in range(B)], np.int32)
+        else:
+            n_phys = B * n_log + 3
+            perm = rng.permutation(n_phys)[:B * n_log]
+            table = perm.reshape(B, n_log).astype(np.int32)
+        pool_k = np.zeros((n_phys, Hkv, page_size, D), np.float32)
+        pool_v = np.zeros_like(pool_k)
+        kp = np.zeros((B, Hkv, n_log * page_size, D), np.float32)
+        vp = np.zeros_like(kp)
+        kp[:, :, :S], vp[:, :, :S] = k, v
+        for b in range(B):
+            # the pages a cache filled to lens[b] has written, in order (later
+            # pages overwrite earlier ones in a ring)
+            for p in range(-(-lens[b] // page_size)):
+                pool_k[table[b, p]] = kp[b, :, p * page_size:(p + 1) * page_size]
+                pool_v[table[b, p]] = vp[b, :, p * page_size:(p + 1) * page_size]
+        out, lse, _ = pbs.flex_attn_fwd_paged(qt, _t(pool_k, dtype, dev), _t(pool_v, dtype, dev),
+                                              torch.from_numpy(table).to(dev), S=S, block_mask=bm, score=sspec,
+                                              mask=spec)
+    else:
+        out, lse = pbs.flex_attn_fwd(qt, _t(k, dtype, dev), _t(v, dtype, dev), block_mask=bm, score=sspec, mask=spec)
+    torch.cuda.synchronize()
+    sc = pbs.default_scale(D)
+    out_ref, lse_ref = attention(_w(q, dtype), _w(k, dtype), _w(v, dtype), scale=sc, score=smod, mask=mod,
+                                 q_offset=offs, kv_len=lens)
+    assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
+
+
+def test_per_batch_offsets_and_lengths_prefill(dev):
+    for dtype, D in (("bf16", 64), ("bf16", 128), ("f32", 64)):
+        run(dev, seed=1, dtype=dtype, B=3, Hq=4, Hkv=2, L=150, S=400, D=D, qb=64, kb=64,
+            score=dict(kind="softcap_alibi", cap=20.0), kind="causal", offs=[250, 0, 40], lens=[400, 130, 230],
+            what=f"prefill {dtype} D={D}")
+    run(dev, seed=2, dtype="bf16", B=2, Hq=2, Hkv=2, L=100, S=300, D=64, qb=128, kb=64, score=dict(kind="none"),
+        kind="noop", offs=[0, 0], lens=[300, 77], what="noop lengths")
+
+
+def test_decode_capacity_example(dev):
+    # the decode section's example scaled to one query per batch: capacity
+    # 8, filled 6, logical position 5, window 3
+    run(dev, seed=3, dtype="bf16", B=2, Hq=4, Hkv=4, L=1, S=8, D=64, qb=16, kb=64, score=dict(kind="none"),
+        kind="causal_window_sinks", window=3, offs=[5, 2], lens=[6, 3], what="capacity 8 filled 6")
+
+
+def test_decode_kernel_per_batch(dev):
+    # 16-query verify steps under GQA: the split-KV decode kernel
+    run(dev, seed=4, dtype="bf16", B=4, Hq=16, Hkv=4, L=16, S=4096, D=128, qb=16, kb=64,
+        score=dict(kind="softcap", cap=50.0), kind="causal", offs=[4080, 1000, 2047, 16], lens=[4096, 1016, 2063, 32],
+        what="decode per batch")
+
+
+@pytest.mark.parametrize("dtype,D,L,page", [("bf16", 128, 16, 64), ("bf16", 64, 200, 128), ("f32", 64, 70, 64)])
+def test_paged_cache(dev, dtype, D, L, page):
+    run(dev, seed=5 + D + L, dtype=dtype, B=3, Hq=8, Hkv=2, L=L, S=1000, D=D, qb=16 if L == 16 else 64, kb=64,
+        score=dict(kind="softcap_alibi", cap=30.0), kind="causal", offs=[1000 - L, 500, 300],
+        lens=[1000, 500 + L, 300 + L], page_size=page, what=f"paged {dtype} D={D} L={L} page={page}")
+
+
+def test_circular_buffer(dev):
+    # a ring of four 64-key pages per batch; the window keeps every visible key
+    # inside the last four pages, whose slots hold the latest writes
+    run(dev, seed=9, dtype="bf16", B=2, Hq=8, Hkv=2, L=16, S=1000, D=128, qb=16, kb=64,
+        score=dict(kind="softcap", cap=50.0), kind="causal_window_sinks", window=150, sinks=0,
+        offs=[984, 700], lens=[1000, 716], page_size=64, ring_pages=4, what="ring of 4 pages")
