@@ -20,7 +20,11 @@ products of 2*D each; the query-major pass recomputes S and dP, which is not
 counted).  The roofline entry then times the backward call (row pass,
 key-major and query-major passes) against its 10*D per cell.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+With --paged PAGE_SIZE the K/V caches are first scattered into a pool of
+pages in a seeded random order and the forward reads them through the page
+table (flex_attn_fwd_paged); everything else is the same.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--paged N]
 """
 import argparse
 import json
@@ -47,6 +51,9 @@ def parse():
     p.add_argument("--workload", default="causal_softcap_alibi")
     p.add_argument("--pass", dest="direction", choices=("fwd", "bwd"), default="fwd",
                    help="fwd: the forward hot path (default); bwd: forward + backward training pass")
+    p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
+                   help="keep K/V in a paged pool of PAGE_SIZE-key pages (seeded random page order) and run the "
+                        "paged forward")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
@@ -168,15 +175,43 @@ def main():
 
     bm_step = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
 
+    def attend(block_mask):
+        pbs.flex_attn_fwd(q, k, v, block_mask=block_mask, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
+
+    if args.paged:
+        # a pool of pages holding every batch's cache, in a seeded random page
+        # order; logical page p of batch b sits in pool page table[b, p]
+        ps = args.paged
+        n_log = -(-w.S // ps)
+        perm = torch.from_numpy(np.random.Generator(np.random.PCG64(w.seed + 77)).permutation(w.B * n_log)
+                                .astype(np.int64)).to(dev)
+        table = perm.view(w.B, n_log).to(torch.int32).contiguous()
+
+        def to_pool(x):
+            xp = torch.zeros((w.B, w.Hkv, n_log * ps, w.D), dtype=x.dtype, device=dev)
+            xp[:, :, :w.S] = x
+            pages = xp.view(w.B, w.Hkv, n_log, ps, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * n_log, w.Hkv, ps, w.D)
+            pool = torch.empty_like(pages)
+            pool[perm] = pages
+            return pool
+        k_pool, v_pool = to_pool(k), to_pool(v)
+        del k, v
+        torch.cuda.synchronize()
+        print(f"bench: paged K/V, {w.B * n_log} pages of {ps} keys", file=sys.stderr, flush=True)
+
+        def attend(block_mask):
+            pbs.flex_attn_fwd_paged(q, k_pool, v_pool, table, S=w.S, block_mask=block_mask, score=sspec, mask=mspec,
+                                    out=out, lse=lse, workspace=ws)
+
     def fwd():
-        pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
+        attend(bm)
 
     def build_only():
         pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, out=bm_step)
 
     def step():
         build_only()
-        pbs.flex_attn_fwd(q, k, v, block_mask=bm_step, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
+        attend(bm_step)
 
     def timed(fn, n):
         stream = torch.cuda.current_stream(dev)
@@ -238,6 +273,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "attn_fwd_decode + attn_fwd_combine" if ws_bytes else "attn_fwd_prefill"
+    if args.paged:
+        roof["traffic"] = None          # counters are taken on the contiguous layout
     roof["algorithmic_per_launch"] = flops if roof["unit"] == "TFLOP/s" else alg_bytes
 
     result = {
@@ -245,17 +282,17 @@ def main():
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) inputs, PCG64 seed %d)" % w.seed,
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "D": w.D,
+        "config": {"workload": w.name + (f"_paged{args.paged}" if args.paged else ""), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "D": w.D,
                    "mask": w.mask, "score": w.score, "cap": w.cap, "window": w.window, "sinks": w.sinks,
                    "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset,
-                   "doc_lengths": inp["doc_lengths"]},
+                   "doc_lengths": inp["doc_lengths"], "page_size": args.paged or None},
         "roofline": roof,
         "fwd_ms": ms_fwd, "blockmask_ms": ms_mask, "launch_mode": mode,
         "fwd_tflops_visited": fwd_tflops, "pct_bf16_peak_fwd": 100.0 * fwd_tflops / BF16_PEAK_TFLOPS,
         "visited_block_flops": flops, "algorithmic_bytes": alg_bytes,
         "hbm_gbs_fwd": alg_bytes / (ms_fwd * 1e-3) / 1e9,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.paged:
         result.update(cpu_baseline(args, w, inp, out, lse, flops))
     print(json.dumps(result), flush=True)
 
