@@ -39,11 +39,14 @@ def score_derivative(score: ScoreMod, s):
     return np.ones_like(s)
 
 
-def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int, pairs=None):
+def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int, pairs=None,
+                       row_chunk: int = 0):
     """(dq, dk, dv) in float64 for (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values.
 
     ``pairs``: optional list of (batch, query head) to include; the gradients
     then hold only those heads' terms (the others stay zero).  Default: all.
+    ``row_chunk``: process that many query rows at a time (0: all); rows are
+    independent, so this only bounds memory, and dk, dv add the chunks' terms.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -59,25 +62,29 @@ def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: Ma
     kv = np.arange(S, dtype=np.int64)[None, :]
     if pairs is None:
         pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    step = row_chunk or L
     for b, h in pairs:
         hk = h // group
         K, V = k[b, hk], v[b, hk]
-        s = (q[b, h] @ K.T) * float(scale)
-        vis = mask(b, h, q_pos, kv)
-        z = np.where(vis, score(s, b, h, q_pos, kv, Hq), -np.inf)
-        live = vis.any(axis=1)
-        P = np.zeros_like(z)
-        if live.any():
-            zl = z[live]
-            e = np.exp(zl - zl.max(axis=1, keepdims=True))
-            P[live] = e / e.sum(axis=1, keepdims=True)
-        O = P @ V
-        dO = dout[b, h]
-        dP = dO @ V.T
-        Dr = (dO * O).sum(axis=1, keepdims=True)
-        dZ = P * (dP - Dr)
-        dS = dZ * score_derivative(score, s) * float(scale)
-        dq[b, h] = dS @ K
-        dk[b, hk] += dS.T @ q[b, h]
-        dv[b, hk] += P.T @ dO
+        for r0 in range(0, L, step):
+            rows = slice(r0, min(L, r0 + step))
+            qp = q_pos[rows]
+            s = (q[b, h, rows] @ K.T) * float(scale)
+            vis = mask(b, h, qp, kv)
+            z = np.where(vis, score(s, b, h, qp, kv, Hq), -np.inf)
+            live = vis.any(axis=1)
+            P = np.zeros_like(z)
+            if live.any():
+                zl = z[live]
+                e = np.exp(zl - zl.max(axis=1, keepdims=True))
+                P[live] = e / e.sum(axis=1, keepdims=True)
+            O = P @ V
+            dO = dout[b, h, rows]
+            dP = dO @ V.T
+            Dr = (dO * O).sum(axis=1, keepdims=True)
+            dZ = P * (dP - Dr)
+            dS = dZ * score_derivative(score, s) * float(scale)
+            dq[b, h, rows] = dS @ K
+            dk[b, hk] += dS.T @ q[b, h, rows]
+            dv[b, hk] += P.T @ dO
     return dq, dk, dv

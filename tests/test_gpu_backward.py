@@ -259,3 +259,35 @@ def test_bwd_long_columns_split(dev, dtype, D):
     for mask in (dict(mask_kind="noop"), dict(mask_kind="causal_window_sinks", window=100, sinks=4)):
         run_bwd_case(dev, seed=60 + D, dtype=dtype, B=1, Hq=8, Hkv=1, L=1100, S=1100, D=D, qb=128, kb=64,
                      score=dict(kind="softcap", cap=20.0), what=f"split {dtype} D={D} {mask['mask_kind']}", **mask)
+
+
+@pytest.mark.parametrize("name,pairs", [("window_sinks_gqa", [(1, 20), (1, 21), (1, 22), (1, 23)]),
+                                        ("doc_causal", [(0, 7)])])
+def test_bwd_full_size_d128(dev, name, pairs):
+    """The head-dim-128 workloads at full size (window + sinks under GQA 4;
+    packed documents, 16K tokens), 128x64 tiles as bench.py runs them, checked
+    on sampled slices: for GQA every query head of one K/V head, so that K/V
+    head's dk, dv are complete."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    up = make_upstream(w)
+    q, k, v, doc_t = to_device(w, inp, dev)
+    dout = torch.from_numpy(up["dout_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    mspec, sspec = specs(w, doc_t)
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    bmq = pbs.flex_blockmask_transpose(bm)
+    out, lse = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    dq, dk, dv = pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=bm, block_mask_q=bmq, score=sspec,
+                                   mask=mspec)
+    torch.cuda.synchronize()
+    mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"])
+    smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
+    print(f"[bwd parity] {name}: oracle over {len(pairs)} head(s)", flush=True)
+    ref_q, ref_k, ref_v = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=pbs.default_scale(w.D),
+                                             score=smod, mask=mmod, q_offset=w.q_offset, pairs=pairs, row_chunk=512)
+    b = pairs[0][0]
+    heads = [h for _, h in pairs]
+    hk = heads[0] // (w.Hq // w.Hkv)
+    got = (dq[b, heads].float().cpu().numpy(), dk[b, hk].float().cpu().numpy(), dv[b, hk].float().cpu().numpy())
+    ref = (ref_q[b, heads], ref_k[b, hk], ref_v[b, hk])
+    assert_grads_close(got, ref, "bf16", f"full size {name}")

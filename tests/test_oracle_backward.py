@@ -176,3 +176,13 @@ def test_transposed_lists_brute_force():
                         off_ = [r for r in range(nQB) if cls[b, h, r, c] != tag]
                         assert tq[num][b, h, c] == len(on)
                         assert tq[ind][b, h, c].tolist() == on + off_
+
+
+def test_row_chunks_change_nothing():
+    q, k, v, do = _inputs(21, 2, 4, 2, 37, 29, 8)
+    kw = dict(scale=0.6, score=ScoreMod("softcap_alibi", cap=2.0), mask=MaskMod("causal_window_sinks", window=7,
+                                                                                 sinks=2), q_offset=3)
+    whole = attention_backward(q, k, v, do, **kw)
+    parts = attention_backward(q, k, v, do, row_chunk=5, **kw)
+    for a, b in zip(whole, parts):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
