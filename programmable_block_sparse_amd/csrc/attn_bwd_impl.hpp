@@ -433,7 +433,7 @@ template <typename T, int D> struct DkdvLds {
 };
 
 template <typename T, int D, int SCORE, bool EXT>
-__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_t* lds3) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_t* lds3, int block) {
     using G = BwdTiles<T, D>;
     constexpr bool kDma = sizeof(T) == 2;
 
@@ -446,8 +446,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
     const int per_bh = a.nKB * subs;
     const int BH = a.B * a.Hkv;
     const int items = BH * per_bh;
-    const int split = (int)(blockIdx.x / items);
-    const int n = (int)(blockIdx.x % items);
+    const int split = block / items;
+    const int n = block % items;
     int bh, kt;
     if (items % 8 == 0 && (items / 8) % per_bh == 0) {
         const int hpx = items / 8 / per_bh, k = n >> 3;
@@ -676,7 +676,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
 template <typename T, int D, int SCORE, bool EXT>
 __global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kKeys)) void attn_bwd_dkdv(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[DkdvLds<T, D>::value];
-    dkdv_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds);
+    dkdv_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds, (int)blockIdx.x);
 }
 
 // Adds the split partial sums of the columns the key-major pass cut, in
@@ -716,7 +716,7 @@ template <typename T, int D> struct DqLds {
 };
 
 template <typename T, int D, int SCORE, bool EXT>
-__device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t* lds3) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t* lds3, int block) {
     using G = BwdTiles<T, D>;
     constexpr bool kDma = sizeof(T) == 2;
 
@@ -725,8 +725,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     // forward.
     const int BH = a.B * a.Hq;
     const int parts = a.q_block / 64;
-    const int qb = a.nQB - 1 - (int)(blockIdx.x / (BH * parts));
-    const int rem = (int)(blockIdx.x % (BH * parts));
+    const int qb = a.nQB - 1 - block / (BH * parts);
+    const int rem = block % (BH * parts);
     const int part = rem / BH;
     int bh = rem % BH;
     if (a.group > 1 && BH % (8 * a.group) == 0) {
@@ -873,23 +873,56 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
 template <typename T, int D, int SCORE, bool EXT>
 __global__ __launch_bounds__(kThreads, (BwdOccupancy<T, D>::kRows)) void attn_bwd_dq(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[DqLds<T, D>::value];
-    dq_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds);
+    dq_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds, (int)blockIdx.x);
+}
+
+// Both major passes in one launch: workgroups [0, kv_blocks) take the
+// key-major work, the rest the query-major work, so query-major workgroups
+// run on CUs beside key-major ones instead of after the whole key-major pass
+// (the key-major kernel at head dim 128 spills and waits on memory, which the
+// query-major MFMA work then fills).
+template <typename T, int D> struct FusedOccupancy {
+    static constexpr int value =
+        BwdOccupancy<T, D>::kKeys < BwdOccupancy<T, D>::kRows ? BwdOccupancy<T, D>::kKeys : BwdOccupancy<T, D>::kRows;
+};
+
+template <typename T, int D, int SCORE, bool EXT>
+__global__ __launch_bounds__(kThreads, (FusedOccupancy<T, D>::value)) void attn_bwd_fused(BwdArgs a, int kv_blocks) {
+    __shared__ __attribute__((aligned(16)))
+    char lds[DkdvLds<T, D>::value > DqLds<T, D>::value ? DkdvLds<T, D>::value : DqLds<T, D>::value];
+    if ((int)blockIdx.x < kv_blocks) dkdv_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds, (int)blockIdx.x);
+    else dq_body<T, D, SCORE, EXT>(a, lds, (lds_char_t*)lds, (int)blockIdx.x - kv_blocks);
 }
 
 // ------------------------------------------------------------------ launch
 template <typename T, int D, int SCORE, bool EXT>
 hipError_t launch_bwd_passes(const BwdArgs& a, hipStream_t stream) {
     const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKB * (a.kv_block / kTileN);
+    const int64_t q_items = (int64_t)a.B * a.Hq * a.nQB * (a.q_block / 64);
+    hipError_t e;
+    // one launch for GQA at head dim 128 (bf16, element-rule masks); two
+    // otherwise: at head dim 64 the query-major pass alone runs at a higher
+    // occupancy than in the shared kernel, and without GQA or with program
+    // masks the single launch measured no faster
+    if constexpr (sizeof(T) == 2 && D == 128 && !EXT) {
+        if (a.group > 1) {
+            hipLaunchKernelGGL((attn_bwd_fused<T, D, SCORE, EXT>), dim3((unsigned)(kv_items * a.kv_splits + q_items)),
+                               dim3(kThreads), 0, stream, a, (int)(kv_items * a.kv_splits));
+            e = hipGetLastError();
+            if (e != hipSuccess || a.kv_splits <= 1) return e;
+            hipLaunchKernelGGL((attn_bwd_dkdv_reduce<T, D>), dim3((unsigned)kv_items), dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((attn_bwd_dkdv<T, D, SCORE, EXT>), dim3((unsigned)(kv_items * a.kv_splits)), dim3(kThreads), 0,
                        stream, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.kv_splits > 1) {
         hipLaunchKernelGGL((attn_bwd_dkdv_reduce<T, D>), dim3((unsigned)kv_items), dim3(kThreads), 0, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t q_items = (int64_t)a.B * a.Hq * a.nQB * (a.q_block / 64);
     hipLaunchKernelGGL((attn_bwd_dq<T, D, SCORE, EXT>), dim3((unsigned)q_items), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
