@@ -327,6 +327,18 @@ def graph_runners(runners, dev, check):
     return {name: g.replay for name, g in graphs.items()}
 
 
+def bwd_kernel_names(w) -> str:
+    """Kernels of one backward call: the two major passes share one launch
+    under GQA at head dim 128 (bf16, element-rule masks); long Q-side columns
+    add the split-sum kernel."""
+    fused = w.dtype == "bf16" and w.D == 128 and w.Hq > w.Hkv and w.mask != "program"
+    names = "attn_bwd_rows + " + ("attn_bwd_fused" if fused else "attn_bwd_dkdv + attn_bwd_dq")
+    group, n_qb = w.Hq // w.Hkv, -(-w.L // w.q_block)
+    if group * n_qb * (w.q_block // 64) > 128:
+        names += " + attn_bwd_dkdv_reduce"
+    return names
+
+
 def main_bwd(args):
     import torch
     import programmable_block_sparse_amd as pbs
@@ -409,7 +421,7 @@ def main_bwd(args):
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     bwd_tflops = bwd_flops / (ms_bwd * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": bwd_tflops, "peak": peak, "unit": "TFLOP/s", "frac": bwd_tflops / peak,
-            "traffic": None, "kernel": "attn_bwd_rows + attn_bwd_dkdv + attn_bwd_dq",
+            "traffic": None, "kernel": bwd_kernel_names(w),
             "algorithmic_per_launch": bwd_flops}
     result = {
         "metric": "flex fwd+bwd TFLOP/s (visited-block FLOPs: 4*D fwd + 10*D bwd per cell)",
