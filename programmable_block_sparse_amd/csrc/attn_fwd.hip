@@ -23,14 +23,17 @@ ScoreConsts score_consts(float scale_f, float cap_f, int score_kind) {
 }
 
 // Row layout of the prefill kernel: 64-row workgroups with key halves split
-// across waves when the 128-row work items are too few to fill the chip at
-// three workgroups per CU or when one Q block row dominates (causal masks), else
-// 128-row workgroups (each K/V tile staged in LDS then serves twice the rows).
+// across waves when the 128-row work items are too few to fill the chip, else
+// 128-row workgroups (each K/V tile staged in LDS then serves twice the rows,
+// and a wave's two key halves overlap one's QK^T with the other's softmax).
+// Head dim 128: 128-row items from three per slot at two workgroups per CU;
+// bf16 head dim 64: from one per slot at three per CU; fp32 head dim 64
+// always splits.
 int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D) {
-    (void)dtype;
     if (q_block <= 64) return 1;
     const int64_t items = (int64_t)B * Hq * nQB;
-    return (D == 64 || items < 2 * 256 * 3) ? 1 : 0;
+    if (D == 64) return (dtype != 1 || items < 256 * 3) ? 1 : 0;
+    return items < 2 * 256 * 3 ? 1 : 0;
 }
 
 int decode_splits(int dtype, int B, int Hq, int Hkv, int L, int D, int q_block, int kv_block, int nKB, int Hm) {

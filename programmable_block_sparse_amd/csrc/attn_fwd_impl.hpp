@@ -635,16 +635,18 @@ __device__ __forceinline__ void apply_mask(float (&z)[16], const MaskArgs& m, in
     }
 }
 
-// One 32-key half (kb2) of a 64-key tile: QK^T, score_mod, the element mask on
-// partial tiles (wave-uniform branch), softmax update, PV.  The two halves of
-// every tile go to two different waves that own the same query rows; their
-// partial states are merged once at the end (merge_key_halves).
-template <typename T, int D, int SCORE, bool FIXED, bool EXT>
-__device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* __restrict__ buf,
-                                             const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
-                                             RowState<Precise<T>::value>& st, const TileConsts& tc,
-                                             const MaskArgs& mask, bool masked, int kv0, int S, const LaneRow& row,
-                                             int kb2, int kb2_lds, int lane) {
+// One 32-key half (kb2) of a 64-key tile after QK^T: score_mod, the element
+// mask on partial tiles (wave-uniform branch), softmax update, PV with the V
+// tile and document ids in buf.  mid() runs between the mask and the
+// exponentials, so that work placed there (QK^T of the tile's other key half)
+// shares a basic block with the exponentials and PV and its MFMAs overlap
+// their VALU work.
+template <typename T, int D, int SCORE, bool FIXED, bool EXT, typename Mid>
+__device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __restrict__ buf,
+                                            const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
+                                            RowState<Precise<T>::value>& st, const TileConsts& tc,
+                                            const MaskArgs& mask, bool masked, int kv0, int S, const LaneRow& row,
+                                            int kb2, int kb2_lds, int lane, Mid&& mid) {
     using G = Tiles<T, D>;
     constexpr bool P = Precise<T>::value;
     using RefT = typename std::conditional<P, double, float>::type;
@@ -652,7 +654,6 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
     const T* Vs = reinterpret_cast<const T*>(buf) + G::kElemsK;
     const int* doc_lds = reinterpret_cast<const int*>(buf + G::kDocOffset);
     {
-        const f32x16_t s = qk_block<T, D>(qr, buf, la, sizeof(T) == 2 ? kb2_lds : kb2, lane);
         float z[16];
         const RefT ref_sub = FIXED ? (RefT)tc.ref_fixed : ((st.ref == (RefT)kNegInf) ? (RefT)0 : st.ref);
         const int key_base = kv0 + 32 * kb2 + 4 * hf;
@@ -748,6 +749,7 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
             }
         }
 
+        mid();
         float lsum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -766,6 +768,36 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
             pv_bf16<D>(o, pb, reinterpret_cast<const char*>(Vs), la, kb2_lds);
         }
     }
+}
+
+// One 32-key half (kb2) of a 64-key tile: QK^T, then tile_update.  The two
+// halves of every tile go to two different waves that own the same query
+// rows (their partial states are merged once at the end, merge_key_halves),
+// or both to one wave (process_tile_pair).
+template <typename T, int D, int SCORE, bool FIXED, bool EXT>
+__device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* __restrict__ buf,
+                                             const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
+                                             RowState<Precise<T>::value>& st, const TileConsts& tc,
+                                             const MaskArgs& mask, bool masked, int kv0, int S, const LaneRow& row,
+                                             int kb2, int kb2_lds, int lane) {
+    const f32x16_t s = qk_block<T, D>(qr, buf, la, sizeof(T) == 2 ? kb2_lds : kb2, lane);
+    tile_update<T, D, SCORE, FIXED, EXT>(s, buf, la, o, st, tc, mask, masked, kv0, S, row, kb2, kb2_lds, lane,
+                                         [] {});
+}
+
+// Both 32-key halves of a 64-key tile in one wave: QK^T of the second half is
+// issued inside the first half's exponential/PV block.
+template <typename T, int D, int SCORE, bool FIXED, bool EXT>
+__device__ __forceinline__ void process_tile_pair(const QRegs<T, D>& qr, const char* __restrict__ buf,
+                                                  const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
+                                                  RowState<Precise<T>::value>& st, const TileConsts& tc,
+                                                  const MaskArgs& mask, bool masked, int kv0, int S,
+                                                  const LaneRow& row, int lane) {
+    const f32x16_t s0 = qk_block<T, D>(qr, buf, la, 0, lane);
+    f32x16_t s1;
+    tile_update<T, D, SCORE, FIXED, EXT>(s0, buf, la, o, st, tc, mask, masked, kv0, S, row, 0, 0, lane,
+                                         [&] { s1 = qk_block<T, D>(qr, buf, la, 1, lane); });
+    tile_update<T, D, SCORE, FIXED, EXT>(s1, buf, la, o, st, tc, mask, masked, kv0, S, row, 1, 1, lane, [] {});
 }
 
 // Calls f(integral_constant<int, I>) for I = FIRST .. LAST - 1.
@@ -877,8 +909,8 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
                 process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, kh, 0,
                                                       lane);
             } else {
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 0, 0, lane);
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, 1, 1, lane);
+                process_tile_pair<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row,
+                                                                lane);
             }
         }
     };
@@ -1302,8 +1334,8 @@ template <typename T, int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const int rows = a.ksplit ? 64 : 128;
     const int64_t blocks = (int64_t)a.nQB * ((a.q_block + rows - 1) / rows) * a.B * a.Hq;
-    if constexpr (D == 64) {
-        // head dim 64 always uses key-split workgroups (prefill_ksplit)
+    if constexpr (D == 64 && sizeof(T) == 4) {
+        // fp32 at head dim 64 always uses key-split workgroups (prefill_ksplit)
         if (!a.ksplit) return hipErrorInvalidValue;
         hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, a);
