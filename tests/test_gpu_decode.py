@@ -107,6 +107,14 @@ def test_paged_cache(dev, dtype, D, L, page):
         lens=[1000, 500 + L, 300 + L], page_size=page, what=f"paged {dtype} D={D} L={L} page={page}")
 
 
+def test_paged_cache_128_row_workgroups(dev):
+    """A paged prefill large enough (B*Hq*ceil(L/128) = 768 row blocks) for
+    the 128-row workgroups at head dim 64, with per-batch offsets and lengths."""
+    run(dev, seed=31, dtype="bf16", B=3, Hq=128, Hkv=32, L=200, S=700, D=64, qb=128, kb=64,
+        score=dict(kind="softcap_alibi", cap=30.0), kind="causal", offs=[500, 120, 0], lens=[700, 320, 200],
+        page_size=128, what="paged bf16 D=64 128-row workgroups")
+
+
 def test_circular_buffer(dev):
     # a ring of four 64-key pages per batch; the window keeps every visible key
     # inside the last four pages, whose slots hold the latest writes

@@ -414,6 +414,23 @@ def test_attention_program_masks(dev, dtype, D):
                  what=f"{dtype} D={D} {name} {score}")
 
 
+@pytest.mark.parametrize("case", ["softcap_alibi_causal", "none_noop", "softcap_doc", "alibi_program", "max_window"])
+def test_attention_128_row_workgroups_d64(dev, case):
+    """bf16 at head dim 64 with B*Hq*ceil(L/128) >= 768 row blocks, enough
+    that the prefill takes 128-row workgroups in which each wave computes
+    both key halves of a tile (QK^T of the second half overlapping the first
+    half's softmax).  Ragged L and S, GQA 4, every output checked."""
+    score, mask = {
+        "softcap_alibi_causal": (dict(kind="softcap_alibi", cap=30.0, alibi_m=8.0), dict(mask_kind="causal")),
+        "none_noop": (dict(kind="none"), dict(mask_kind="noop")),
+        "softcap_doc": (dict(kind="softcap", cap=5.0), dict(mask_kind="doc_causal")),
+        "alibi_program": (dict(kind="alibi", alibi_m=8.0), dict(mask_kind="program", clauses=PROGRAMS["prefix_lm"])),
+        "max_window": (dict(kind="softcap", cap=20.0), dict(mask_kind="causal_window_sinks", window=90, sinks=2)),
+    }[case]
+    run_case(dev, seed=700 + len(case), dtype="bf16", B=2, Hq=128, Hkv=32, L=300, S=333, D=64, qb=128, kb=64,
+             score=score, with_max=case == "max_window", what=f"128-row workgroups D=64 {case}", **mask)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 128)])
 def test_plain_alibi_score(dev, dtype, D):
     for i, mask in enumerate(MASKS):
