@@ -310,22 +310,19 @@ __global__ __launch_bounds__(build_threads<KIND>()) void blockmask_build(BuildAr
         }
     }
 
-    // Phase 1: classify.  Corner rules first (sixteen tiles per thread), then
-    // the tiles that need counting, one per wave.
+    // Phase 1: classify.  Corner rules first (one tile per thread, the 2-bit
+    // classes OR-ed into their LDS words), then the tiles that need counting,
+    // one per wave.
     const int words = (a.nKB + 15) >> 4;
-    for (int w = threadIdx.x; w < words; w += kBuildThreads) {
-        uint32_t word = 0;
-        for (int t = 0; t < 16; ++t) {
-            const int kb = w * 16 + t;
-            if (kb >= a.nKB) break;
-            const int c0 = kb * a.kv_block;
-            const int c1 = min(c0 + a.kv_block, S) - 1;
-            const bool clipped = rows < a.q_block || c0 + a.kv_block > S;
-            // tiles past the valid keys are empty
-            const int cls = c0 >= S ? TILE_EMPTY : corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped, h);
-            word |= (uint32_t)cls << (2 * t);
-        }
-        tile_class[w] = word;
+    for (int w = threadIdx.x; w < words; w += kBuildThreads) tile_class[w] = 0u;
+    __syncthreads();
+    for (int kb = threadIdx.x; kb < a.nKB; kb += kBuildThreads) {
+        const int c0 = kb * a.kv_block;
+        const int c1 = min(c0 + a.kv_block, S) - 1;
+        const bool clipped = rows < a.q_block || c0 + a.kv_block > S;
+        // tiles past the valid keys are empty
+        const int cls = c0 >= S ? TILE_EMPTY : corner_class<KIND>(a.mask, p0, p1, c0, c1, clipped, h);
+        if (cls != 0) atomicOr(&tile_class[kb >> 4], (uint32_t)cls << (2 * (kb & 15)));
     }
     __syncthreads();
     if constexpr (KIND == MASK_CAUSAL_WINDOW_SINKS || KIND == MASK_DOC_CAUSAL || KIND == MASK_PROGRAM) {
