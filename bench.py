@@ -72,22 +72,30 @@ KERNEL_SOURCES = ("programmable_block_sparse_amd/csrc/attn_fwd.hip",
                   "programmable_block_sparse_amd/csrc/attn_fwd_f32_d128.hip",
                   "programmable_block_sparse_amd/csrc/device_common.hpp",
                   "programmable_block_sparse_amd/csrc/internal.hpp")
+# the backward kernels include the forward's device code
+KERNEL_SOURCES_BWD = KERNEL_SOURCES + ("programmable_block_sparse_amd/csrc/attn_bwd.hip",
+                                       "programmable_block_sparse_amd/csrc/attn_bwd_impl.hpp",
+                                       "programmable_block_sparse_amd/csrc/attn_bwd_bf16_d64.hip",
+                                       "programmable_block_sparse_amd/csrc/attn_bwd_bf16_d128.hip",
+                                       "programmable_block_sparse_amd/csrc/attn_bwd_f32_d64.hip",
+                                       "programmable_block_sparse_amd/csrc/attn_bwd_f32_d128.hip")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per forward launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary of this workload, or None when there is none or the kernel sources
-    changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+def measured_traffic(workload, backward=False):
+    """HBM bytes per forward launch (per backward call with backward=True)
+    from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload, or
+    None when there is none or the kernel sources changed since it was taken."""
+    name = f"hbm_traffic_bwd_{workload}.txt" if backward else f"hbm_traffic_{workload}.txt"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -96,7 +104,7 @@ def measured_traffic(workload):
             if ":" in line and not line.startswith(" "):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(KERNEL_SOURCES_BWD if backward else KERNEL_SOURCES):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -421,7 +429,7 @@ def main_bwd(args):
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     bwd_tflops = bwd_flops / (ms_bwd * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": bwd_tflops, "peak": peak, "unit": "TFLOP/s", "frac": bwd_tflops / peak,
-            "traffic": None, "kernel": bwd_kernel_names(w),
+            "traffic": measured_traffic(w.name, backward=True), "kernel": bwd_kernel_names(w),
             "algorithmic_per_launch": bwd_flops}
     result = {
         "metric": "flex fwd+bwd TFLOP/s (visited-block FLOPs: 4*D fwd + 10*D bwd per cell)",
