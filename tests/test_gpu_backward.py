@@ -201,9 +201,16 @@ def test_bwd_programs(dev, pi):
                      bm_heads=heads, what=f"program {pi} {dtype}")
 
 
-def test_bwd_deterministic(dev):
-    kw = dict(seed=5, dtype="bf16", B=2, Hq=8, Hkv=2, L=300, S=300, D=64, qb=128, kb=64,
-              score=dict(kind="softcap_alibi", cap=30.0), mask_kind="causal", what="det")
+@pytest.mark.parametrize("D,L,sinks", [(64, 300, 0), (128, 300, 0), (128, 1100, 4)])
+def test_bwd_deterministic(dev, D, L, sinks):
+    """Two runs give bitwise equal gradients: every dq row and every dk, dv
+    key is written by one workgroup and split sums are added in a fixed order.
+    Head dim 128 under GQA takes the single shared launch; L = 1100 with sinks
+    under GQA 8 adds long Q-side columns cut into shares."""
+    kw = dict(seed=5, dtype="bf16", B=2, Hq=8, Hkv=1 if sinks else 2, L=L, S=L, D=D, qb=128, kb=64,
+              score=dict(kind="softcap_alibi", cap=30.0),
+              mask_kind="causal_window_sinks" if sinks else "causal", window=128, sinks=sinks,
+              what=f"det D={D} L={L} sinks={sinks}")
     a = run_bwd_case(dev, **kw)
     b = run_bwd_case(dev, **kw)
     for x, y in zip(a, b):
