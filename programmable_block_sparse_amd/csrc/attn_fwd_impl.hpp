@@ -1108,9 +1108,47 @@ template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
 
 
 
+// The Q block of rank j in a longest-first order of the row blocks of mask
+// row 0 that keeps packed documents together.  Under a packed-document mask
+// a document's row blocks have non-decreasing tile counts, so each block is
+// keyed by the count at the end of its non-decreasing run (about its
+// document's length) and blocks are ordered by that key, largest first, then
+// by higher block index.  Long documents run first, each with its blocks
+// together (they share its K/V tiles in L2), and short ones fill the tail.
+// The ranks are a permutation of 0 .. nQB-1, so exactly one block matches.
+// Every thread returns it; uses the first 8 * nQB + 4 bytes of lds.
+__device__ __forceinline__ int longest_first_block(const FwdArgs& a, int j, char* lds) {
+    int* cnt = reinterpret_cast<int*>(lds);
+    int* key = cnt + a.nQB;
+    int* pick = key + a.nQB;
+    for (int q = threadIdx.x; q < a.nQB; q += kThreads)
+        cnt[q] = min(max(a.kv_num[q], 0), a.nKB) + min(max(a.full_num[q], 0), a.nKB);
+    __syncthreads();
+    for (int q = threadIdx.x; q < a.nQB; q += kThreads) {
+        int r = q;
+        while (r + 1 < a.nQB && cnt[r + 1] >= cnt[r]) ++r;
+        key[q] = cnt[r];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < a.nQB; q += kThreads) {
+        const int c = key[q];
+        int rank = 0;
+        for (int q2 = 0; q2 < a.nQB; ++q2) {
+            const int c2 = key[q2];
+            rank += (c2 > c || (c2 == c && q2 > q)) ? 1 : 0;
+        }
+        if (rank == j) *pick = q;
+    }
+    __syncthreads();
+    const int qb = *pick;
+    __syncthreads();   // the tile walk reuses lds
+    return qb;
+}
+
 // Prefill: one workgroup per (row part of a Q block, query head, batch),
 // highest Q block index first (under causal-type masks it holds the most
-// tiles).  KSPLIT: a part is 64 rows and wave w handles row group w & 1 (32
+// tiles), or longest document first (longest_first: packed documents).
+// KSPLIT: a part is 64 rows and wave w handles row group w & 1 (32
 // rows) and key half w >> 1 of every tile, which halves the tile loop of a
 // workgroup (short critical path when a few Q blocks hold most of the work);
 // otherwise a part is 128 rows, one 32-row group per wave, both key halves.
@@ -1121,7 +1159,8 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT>::val
     constexpr int kRows = KSPLIT ? 64 : 128;
     const int BH = a.B * a.Hq;
     const int parts = (a.q_block + kRows - 1) / kRows;
-    const int qb = a.nQB - 1 - (int)(blockIdx.x / (BH * parts));
+    const int order = (int)(blockIdx.x / (BH * parts));
+    const int qb = a.longest_first ? longest_first_block(a, order, lds) : a.nQB - 1 - order;
     const int rem = (int)(blockIdx.x % (BH * parts));
     const int part = rem / BH;
     int bh = rem % BH;

@@ -400,6 +400,13 @@ static flex_status fwd_common(const void* q, const void* k, const void* v, int32
     a.max_pages = pages ? pages->max_pages : 0;
     a.num_pages = pages ? pages->num_pages : 0;
     a.ksplit = prefill_ksplit(dtype, B, Hq, bm->num_q_blocks, bm->q_block, D);
+    // Packed documents give Q blocks tile counts that do not follow the block
+    // index; launching the longest documents first shortens the tail of the
+    // grid.  Not for mask programs: on the chunked workload a longest-first
+    // order spread the resident blocks over every chunk and was 3.5 % slower.
+    // One shared list of row blocks only (B = H = 1 masks).
+    a.longest_first = mask->kind == FLEX_MASK_DOC_CAUSAL && bm->B == 1 && bm->H == 1 &&
+                      bm->num_q_blocks <= kLongestFirstMaxBlocks;
     a.splits = decode_splits(dtype, B, Hq, Hkv, (int)L, D, bm->q_block, bm->kv_block, bm->num_kv_blocks, bm->H);
     a.ws_acc = nullptr;
     a.ws_ml = nullptr;

@@ -108,6 +108,9 @@ struct FwdArgs {
     float ref_fixed;
     // prefill row layout: 1 = 64-row workgroups, key halves split across waves
     int ksplit;
+    // prefill launch order: 1 = Q blocks of mask row 0 by tile count, largest
+    // first (ties: higher block first); 0 = by block index, highest first
+    int longest_first;
     // paged K/V pool (page_table == NULL: contiguous (B, Hkv, S, D) caches):
     // k, v point at pools of num_pages pages, k_sb / v_sb the page strides;
     // page_table[b][p] is the physical page of logical page p of batch b
@@ -123,6 +126,8 @@ struct FwdArgs {
 
 // Prefill row layout for these sizes (see attn_fwd.hip): 1 = key-split.
 int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D);
+// Largest Q blocks rank that the prefill still orders by tile count in-kernel.
+constexpr int kLongestFirstMaxBlocks = 256;
 
 // Number of key-range splits of the GQA-packed decode kernel for these sizes,
 // or 0 when the prefill kernel is used.
