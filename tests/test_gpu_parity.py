@@ -196,6 +196,42 @@ def test_attention_gqa_ratios(dev, G):
              what=f"G={G}")
 
 
+def _many_docs(rng, n, hi):
+    """Document ids of n positions cut into documents of 1..hi tokens."""
+    lens = []
+    while sum(lens) < n:
+        lens.append(int(rng.integers(1, hi + 1)))
+    lens[-1] -= sum(lens) - n
+    return np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+
+
+@pytest.mark.parametrize("D,qb,L", [(64, 128, 3000), (128, 128, 2100), (64, 64, 4200)])
+def test_packed_documents_launch_order(dev, D, qb, L):
+    """Many short documents whose boundaries fall inside Q blocks, so tile
+    counts rise and fall along the sequence.  The prefill launches the Q blocks
+    longest document first; every block must still be computed exactly once.
+    Covers 128-row workgroups (D 64 and 128) and 64-row key-split ones (qb=64,
+    66 blocks)."""
+    rng = np.random.default_rng(900 + D + qb)
+    Hq, Hkv = 2, 1
+    q = rng.standard_normal((1, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((1, Hkv, L, D), dtype=np.float32)
+    v = rng.standard_normal((1, Hkv, L, D), dtype=np.float32)
+    doc_np = _many_docs(rng, L, 400)
+    doc_t = torch.from_numpy(doc_np).to(dev)
+    mspec, mmod = _mask_pair("doc_causal", 0, 0, 0, doc_np, doc_t)
+    bm = pbs.flex_blockmask_build(mspec, L, L, qb, 64, device=dev)
+    print(f"[parity] packed documents D={D} qb={qb} L={L}: {int(doc_np[-1]) + 1} documents, "
+          f"{bm.kv_num_blocks.shape[-1]} Q blocks", flush=True)
+    out, lse = pbs.flex_attn_fwd(_tensor(q, "bf16", dev), _tensor(k, "bf16", dev), _tensor(v, "bf16", dev),
+                                 block_mask=bm, mask=mspec)
+    torch.cuda.synchronize()
+    out_ref, lse_ref, _ = attention(_widen(q, "bf16"), _widen(k, "bf16"), _widen(v, "bf16"),
+                                    scale=pbs.default_scale(D), score=ScoreMod("none"), mask=mmod, q_offset=0,
+                                    with_max=True)
+    assert_attention_close(out, lse, out_ref, lse_ref, "bf16", f"packed documents D={D} qb={qb}")
+
+
 def test_attention_empty_rows_and_offsets(dev):
     # L > S bottom-right: the first L - S rows see no key -> out 0, lse -inf
     run_case(dev, seed=3, dtype="bf16", B=1, Hq=2, Hkv=2, L=200, S=70, D=64, qb=64, kb=64,
