@@ -74,8 +74,17 @@ def assert_grads_close(got, ref, dtype, what):
     print(f"[bwd parity] {what}: " + "; ".join(worst))
 
 
+def _many_docs(rng, n, hi):
+    """Document ids of n positions cut into documents of 1..hi tokens."""
+    lens = []
+    while sum(lens) < n:
+        lens.append(int(rng.integers(1, hi + 1)))
+    lens[-1] -= sum(lens) - n
+    return np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+
+
 def run_bwd_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_kind, window=0, sinks=0,
-                 q_offset=None, clauses=(), bm_heads=1, scale=None, what=""):
+                 q_offset=None, clauses=(), bm_heads=1, scale=None, what="", doc_max=0):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
@@ -85,7 +94,8 @@ def run_bwd_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_k
     clauses = tuple(tuple(c) for c in clauses)
     doc_np = doc_t = None
     if mask_kind == "doc_causal" or any(n == "doc" for c in clauses for n, _ in c):
-        doc_np = _rand_doc(rng, max(S, off + L))
+        n = max(S, off + L)
+        doc_np = _many_docs(rng, n, doc_max) if doc_max else _rand_doc(rng, n)
         doc_t = torch.from_numpy(doc_np).to(dev)
     mspec = pbs.MaskSpec(kind=mask_kind, window=window, sinks=sinks, q_offset=off, doc_id=doc_t, clauses=clauses)
     mmod = MaskMod(mask_kind, window=window, sinks=sinks, doc_id=doc_np, clauses=clauses)
@@ -266,6 +276,15 @@ def test_bwd_long_columns_split(dev, dtype, D):
     for mask in (dict(mask_kind="noop"), dict(mask_kind="causal_window_sinks", window=100, sinks=4)):
         run_bwd_case(dev, seed=60 + D, dtype=dtype, B=1, Hq=8, Hkv=1, L=1100, S=1100, D=D, qb=128, kb=64,
                      score=dict(kind="softcap", cap=20.0), what=f"split {dtype} D={D} {mask['mask_kind']}", **mask)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_packed_documents(dev, D):
+    """Many short documents whose boundaries fall inside Q blocks and key
+    tiles, so the Q-side and KV-side lists rise and fall along the sequence."""
+    run_bwd_case(dev, seed=950 + D, dtype="bf16", B=1, Hq=2, Hkv=1, L=1500, S=1500, D=D, qb=128, kb=64,
+                 score=dict(kind="none"), mask_kind="doc_causal", q_offset=0, doc_max=300,
+                 what=f"packed documents D={D}")
 
 
 @pytest.mark.parametrize("name,pairs", [("window_sinks_gqa", [(1, 20), (1, 21), (1, 22), (1, 23)]),
