@@ -1115,22 +1115,30 @@ template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
 // document's length) and blocks are ordered by that key, largest first, then
 // by higher block index.  Long documents run first, each with its blocks
 // together (they share its K/V tiles in L2), and short ones fill the tail.
-// The ranks are a permutation of 0 .. nQB-1, so exactly one block matches.
-// Every thread returns it; uses the first 8 * nQB + 4 bytes of lds.
+// Run ends are found through a bitmap of the blocks where a run ends (one
+// ballot per wave), so no thread walks a run.  The ranks are a permutation of
+// 0 .. nQB-1, so exactly one block matches.  Needs nQB <= kThreads; every
+// thread returns the block; uses the first 8 * nQB + 40 bytes of lds.
 __device__ __forceinline__ int longest_first_block(const FwdArgs& a, int j, char* lds) {
     int* cnt = reinterpret_cast<int*>(lds);
     int* key = cnt + a.nQB;
-    int* pick = key + a.nQB;
-    for (int q = threadIdx.x; q < a.nQB; q += kThreads)
-        cnt[q] = min(max(a.kv_num[q], 0), a.nKB) + min(max(a.full_num[q], 0), a.nKB);
+    uint64_t* ends = reinterpret_cast<uint64_t*>(key + a.nQB);     // 8-byte aligned: nQB ints twice
+    int* pick = reinterpret_cast<int*>(ends + kThreads / 64);
+    const int q = threadIdx.x;
+    if (q < a.nQB) cnt[q] = min(max(a.kv_num[q], 0), a.nKB) + min(max(a.full_num[q], 0), a.nKB);
     __syncthreads();
-    for (int q = threadIdx.x; q < a.nQB; q += kThreads) {
-        int r = q;
-        while (r + 1 < a.nQB && cnt[r + 1] >= cnt[r]) ++r;
-        key[q] = cnt[r];
+    const bool end = q < a.nQB && (q + 1 == a.nQB || cnt[q + 1] < cnt[q]);
+    const uint64_t m = __ballot(end);
+    if ((q & 63) == 0) ends[q >> 6] = m;
+    __syncthreads();
+    if (q < a.nQB) {
+        int w = q >> 6;
+        uint64_t mm = ends[w] & (~0ull << (q & 63));
+        while (mm == 0) mm = ends[++w];      // block nQB - 1 always ends a run
+        key[q] = cnt[w * 64 + __builtin_ctzll(mm)];
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < a.nQB; q += kThreads) {
+    if (q < a.nQB) {
         const int c = key[q];
         int rank = 0;
         for (int q2 = 0; q2 < a.nQB; ++q2) {
@@ -1144,6 +1152,7 @@ __device__ __forceinline__ int longest_first_block(const FwdArgs& a, int j, char
     __syncthreads();   // the tile walk reuses lds
     return qb;
 }
+static_assert(kLongestFirstMaxBlocks <= kThreads, "one Q block per thread when ordering documents");
 
 // Prefill: one workgroup per (row part of a Q block, query head, batch),
 // highest Q block index first (under causal-type masks it holds the most

@@ -126,7 +126,8 @@ struct FwdArgs {
 
 // Prefill row layout for these sizes (see attn_fwd.hip): 1 = key-split.
 int prefill_ksplit(int dtype, int B, int Hq, int nQB, int q_block, int D);
-// Largest Q blocks rank that the prefill still orders by tile count in-kernel.
+// Most Q blocks the prefill still orders longest document first (one block
+// per thread of a workgroup).
 constexpr int kLongestFirstMaxBlocks = 256;
 
 // Number of key-range splits of the GQA-packed decode kernel for these sizes,
