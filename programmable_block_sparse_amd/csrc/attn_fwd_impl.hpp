@@ -800,6 +800,19 @@ __device__ __forceinline__ void process_tile_pair(const QRegs<T, D>& qr, const c
     tile_update<T, D, SCORE, FIXED, EXT>(s1, buf, la, o, st, tc, mask, masked, kv0, S, row, 1, 1, lane, [] {});
 }
 
+// True when a wave whose 32 rows start at query position q_lo sees no key of
+// the 32-key half starting at k0 (wave-uniform and conservative): every key
+// is at or past S, above every row's diagonal under a causal-type mask, or
+// (window + sinks) outside every row's window and past the sinks.  Skipping
+// such a half of a partial tile is exact: all its weights are zero.
+__device__ __forceinline__ bool half_dead(const MaskArgs& m, int k0, int S, int q_lo) {
+    if (k0 >= S) return true;
+    const bool causal_kind =
+        m.kind == MASK_CAUSAL || m.kind == MASK_CAUSAL_WINDOW_SINKS || m.kind == MASK_DOC_CAUSAL;
+    if (causal_kind && k0 > q_lo + 31) return true;
+    return m.kind == MASK_CAUSAL_WINDOW_SINKS && k0 >= m.sinks && q_lo - (k0 + 31) >= m.window;
+}
+
 // Calls f(integral_constant<int, I>) for I = FIRST .. LAST - 1.
 template <int FIRST, int LAST> struct Unroll {
     template <class F> __device__ __forceinline__ static void run(F&& f) {
@@ -874,6 +887,9 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
         }
     };
 
+    // first query position of this wave's rows (lane 0 holds the lowest row)
+    const int q_lo = __builtin_amdgcn_readfirstlane(row.q_pos);
+
     // Tile descriptors of the ring (static indices after unrolling).
     int ring_kv0[STAGES];
     bool ring_masked[STAGES];
@@ -905,12 +921,19 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
         const int kv0 = ring_kv0[B];
         const bool masked = ring_masked[B];
         if (wave_active) {
+            // Halves of a partial tile that none of this wave's rows can see are
+            // skipped (element-rule masks; mask programs keep the plain walk,
+            // where the test only cost time).
+            const bool may_skip = !EXT && masked;
             if constexpr (KSPLIT) {
-                process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row, kh, 0,
-                                                      lane);
+                if (!(may_skip && half_dead(a.mask, kv0 + 32 * kh, S, q_lo)))
+                    process_tile<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row,
+                                                              kh, 0, lane);
             } else {
-                process_tile_pair<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S, row,
-                                                                lane);
+                // both halves at once: a lone-half path would cost registers in the common case
+                if (!(may_skip && half_dead(a.mask, kv0, S, q_lo) && half_dead(a.mask, kv0 + 32, S, q_lo)))
+                    process_tile_pair<__bf16, D, SCORE, FIXED, EXT>(qr, cur, la, o, st, tc, a.mask, masked, kv0, S,
+                                                                    row, lane);
             }
         }
     };
