@@ -25,14 +25,14 @@ the formula being checked).  Parity unpinned: NaN/Inf inputs, which the pages
 only say must be checked separately.
 """
 from .mods import ScoreMod, MaskMod, alibi_slope
-from .attention import attention, attention_rows
+from .attention import attention, attention_rows, default_scale
 from .blockmask import (build_block_mask, to_dense, sparsity, visible_cells, transpose_block_mask,
                         slice_block_mask, adjust_block_mask, grid_classes, to_string)
 from .blockwise import blockwise_attention
 from .backward import attention_backward, score_derivative
 
 __all__ = [
-    "ScoreMod", "MaskMod", "alibi_slope", "attention", "attention_rows",
+    "ScoreMod", "MaskMod", "alibi_slope", "attention", "attention_rows", "default_scale",
     "build_block_mask", "to_dense", "sparsity", "visible_cells", "blockwise_attention",
     "transpose_block_mask", "slice_block_mask", "adjust_block_mask", "grid_classes", "to_string",
     "attention_backward", "score_derivative",

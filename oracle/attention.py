@@ -30,6 +30,14 @@ import numpy as np
 from .mods import MaskMod, ScoreMod
 
 
+def default_scale(D: int) -> float:
+    """The default softmax scale 1/sqrt(D), D the head (embedding) dimension
+    (2kiu guide, section 6.2: used when no scale is passed, applied to the
+    scores before the softmax), as the float32 value a caller hands the
+    kernel: 1/sqrt(D) evaluated in float64 and rounded once to float32."""
+    return float(np.float32(1.0 / np.sqrt(np.float64(D))))
+
+
 def _rows_softmax(z: np.ndarray, vis: np.ndarray, V: np.ndarray):
     """Row softmax of z (with -inf where not visible) applied to V; empty rows -> 0, -inf."""
     n_rows = z.shape[0]

@@ -374,7 +374,20 @@ class BlockMask:
     def _stream(self):
         return ctypes.c_void_p(_stream_ptr(self.kv_indices.device))
 
+    def _validate(self, device=None):
+        """The four arrays: int32, contiguous, on ``device`` (default: the mask's
+        own GPU), shapes (B, H, nQB) and (B, H, nQB, nKB) for this mask's L, S."""
+        device = self.kv_indices.device if device is None else device
+        if self.q_block < 1 or self.kv_block < 1:
+            raise ValueError("block sizes must be positive")
+        nqb, nkb = -(-self.L // self.q_block), -(-self.S // self.kv_block)
+        B, H = self.kv_num_blocks.shape[:2] if self.kv_num_blocks.dim() == 3 else (-1, -1)
+        for name, shape in (("kv_num_blocks", (B, H, nqb)), ("kv_indices", (B, H, nqb, nkb)),
+                            ("full_kv_num_blocks", (B, H, nqb)), ("full_kv_indices", (B, H, nqb, nkb))):
+            _require(getattr(self, name), f"block mask {name}", device, dtype=torch.int32, shape=shape)
+
     def to_c(self) -> flex_block_mask:
+        self._validate()
         cached = self.__dict__.get("_c")
         if cached is not None:
             return cached
@@ -388,6 +401,53 @@ class BlockMask:
         c.full_kv_indices = self.full_kv_indices.data_ptr()
         self.__dict__["_c"] = c
         return c
+
+
+def _require(t, name: str, device, *, dtype=None, shape=None, contiguous: bool = True):
+    """Raise ValueError unless ``t`` is a tensor on ``device`` (a GPU) with the
+    given dtype, exact shape and contiguity.  Runs before any pointer is handed
+    to the library, so a wrong buffer is an error, never a stray address."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device} (it is on {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (it is {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (it has {tuple(t.shape)})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _require_workspace(ws, ws_bytes: int, device):
+    if ws is None:
+        return
+    _require(ws, "workspace", device)
+    if ws.numel() * ws.element_size() < ws_bytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {ws_bytes} needed")
+
+
+def _require_mask_tensors(mask: "MaskSpec", device, B: Optional[int]):
+    if mask.doc_id is not None:
+        _require(mask.doc_id, "doc_id", device, dtype=torch.int32)
+        if mask.doc_id.dim() != 1:
+            raise ValueError("doc_id must be 1-D")
+    for name in ("q_offsets", "kv_lens"):
+        t = getattr(mask, name)
+        if t is not None:
+            _require(t, name, device, dtype=torch.int32, shape=None if B is None else (B,))
+
+
+def _require_qkv(q, k, v, names=("q", "k", "v")):
+    """q, k, v (or q and the pools): GPU tensors on one device, last dim
+    contiguous (other strides are passed to the library)."""
+    for t, name in zip((q, k, v), names):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+        if t.stride(3) != 1:
+            raise ValueError("the last dimension must be contiguous")
 
 
 def _stream_ptr(device) -> int:
@@ -409,6 +469,8 @@ def flex_blockmask_build(mask: MaskSpec, L: int, S: int, q_block: int, kv_block:
         out = BlockMask(t(B, H, nqb), t(B, H, nqb, nkb), t(B, H, nqb), t(B, H, nqb, nkb), q_block, kv_block, L, S)
     elif (out.L, out.S, out.q_block, out.kv_block, out.B, out.H) != (L, S, q_block, kv_block, B, H):
         raise ValueError("out BlockMask has different dims")
+    out._validate()
+    _require_mask_tensors(mask, out.kv_indices.device, None)
     cm = mask.to_c(L, S)
     cbm = out.to_c()
     _check(lib.flex_blockmask_build(ctypes.byref(cm), L, S, ctypes.byref(cbm),
@@ -462,23 +524,30 @@ def _fwd(q, k, v, block_mask, score, mask, scale, return_lse, return_max, out, l
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPES:
         raise ValueError("q, k, v must share a dtype, float32 or bfloat16")
-    for t in (q, k, v):
-        if t.stride(3) != 1:
-            raise ValueError("the last dimension must be contiguous")
+    _require_qkv(q, k, v)
+    dev = q.device
     if out is None:
-        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=dev)
+    _require(out, "out", dev, dtype=q.dtype, shape=(B, Hq, L, D))
     if return_lse and lse is None:
-        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _require(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, L))
     if return_max and max_scores is None:
-        max_scores = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+        max_scores = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     if not return_max:
         max_scores = None
+    if max_scores is not None:
+        _require(max_scores, "max_scores", dev, dtype=torch.float32, shape=(B, Hq, L))
+    block_mask._validate(dev)
+    _require_mask_tensors(mask, dev, B)
     cbm = block_mask.to_c()
     ws_bytes = int(lib.flex_attn_fwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
-    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _require_workspace(workspace, ws_bytes, dev)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     cs, cm = score.to_c(), mask.to_c(L, S)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
@@ -505,6 +574,13 @@ class BlockMaskQ:
     L: int
     S: int
 
+    def _validate(self, device, block_mask: "BlockMask"):
+        """int32, contiguous, on ``device``, transposed dims of ``block_mask``."""
+        B, H, nqb, nkb = block_mask.kv_indices.shape
+        for name, shape in (("q_num_blocks", (B, H, nkb)), ("q_indices", (B, H, nkb, nqb)),
+                            ("full_q_num_blocks", (B, H, nkb)), ("full_q_indices", (B, H, nkb, nqb))):
+            _require(getattr(self, name), f"Q-side block mask {name}", device, dtype=torch.int32, shape=shape)
+
     def to_c(self) -> flex_block_mask_q:
         cached = self.__dict__.get("_c")
         if cached is not None:
@@ -530,6 +606,8 @@ def flex_blockmask_transpose(block_mask: BlockMask, out: Optional[BlockMaskQ] = 
         t = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
         out = BlockMaskQ(t(B, H, nkb), t(B, H, nkb, nqb), t(B, H, nkb), t(B, H, nkb, nqb), block_mask.q_block,
                          block_mask.kv_block, block_mask.L, block_mask.S)
+    block_mask._validate()
+    out._validate(block_mask.kv_indices.device, block_mask)
     cbm, cq = block_mask.to_c(), out.to_c()
     _check(lib.flex_blockmask_transpose(ctypes.byref(cbm), ctypes.byref(cq),
                                         ctypes.c_void_p(_stream_ptr(block_mask.kv_indices.device))))
@@ -560,24 +638,28 @@ def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or q.dtype not in DTYPES:
         raise ValueError("q, k, v, out, dout must share a dtype, float32 or bfloat16")
-    for t in (q, k, v):
-        if t.stride(3) != 1:
-            raise ValueError("the last dimension must be contiguous")
-    for t, shape in ((out, (B, Hq, L, D)), (dout, (B, Hq, L, D))):
-        if tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError("out and dout must be contiguous (B, Hq, L, D)")
-    if tuple(lse.shape) != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 (B, Hq, L)")
+    _require_qkv(q, k, v)
+    dev = q.device
+    for t, name in ((out, "out"), (dout, "dout")):
+        _require(t, name, dev, dtype=q.dtype, shape=(B, Hq, L, D))
+    _require(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, L))
     if dq is None:
-        dq = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
+        dq = torch.empty((B, Hq, L, D), dtype=q.dtype, device=dev)
     if dk is None:
-        dk = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
+        dk = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=dev)
     if dv is None:
-        dv = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=q.device)
+        dv = torch.empty((B, Hkv, S, D), dtype=q.dtype, device=dev)
+    _require(dq, "dq", dev, dtype=q.dtype, shape=(B, Hq, L, D))
+    _require(dk, "dk", dev, dtype=q.dtype, shape=(B, Hkv, S, D))
+    _require(dv, "dv", dev, dtype=q.dtype, shape=(B, Hkv, S, D))
+    block_mask._validate(dev)
+    block_mask_q._validate(dev, block_mask)
+    _require_mask_tensors(mask, dev, B)
     cbm, cq = block_mask.to_c(), block_mask_q.to_c()
     ws_bytes = int(lib.flex_attn_bwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
-    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _require_workspace(workspace, ws_bytes, dev)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     cs, cm = score.to_c(), mask.to_c(L, S)
     _check(lib.flex_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
@@ -612,19 +694,26 @@ def flex_attn_fwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Ten
     if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.dim() != 2 \
             or page_table.shape[0] != B:
         raise ValueError("page_table must be a contiguous int32 (B, max_pages) tensor")
-    for t in (q, k_pool, v_pool):
-        if t.stride(3) != 1:
-            raise ValueError("the last dimension must be contiguous")
+    _require_qkv(q, k_pool, v_pool, ("q", "k_pool", "v_pool"))
+    dev = q.device
+    _require(page_table, "page_table", dev, dtype=torch.int32)
     if out is None:
-        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=q.device)
-    lse = (lse if lse is not None else torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)) \
+        out = torch.empty((B, Hq, L, D), dtype=q.dtype, device=dev)
+    _require(out, "out", dev, dtype=q.dtype, shape=(B, Hq, L, D))
+    lse = (lse if lse is not None else torch.empty((B, Hq, L), dtype=torch.float32, device=dev)) \
         if return_lse else None
     max_scores = (max_scores if max_scores is not None else
-                  torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)) if return_max_scores else None
+                  torch.empty((B, Hq, L), dtype=torch.float32, device=dev)) if return_max_scores else None
+    for t, name in ((lse, "lse"), (max_scores, "max_scores")):
+        if t is not None:
+            _require(t, name, dev, dtype=torch.float32, shape=(B, Hq, L))
+    block_mask._validate(dev)
+    _require_mask_tensors(mask, dev, B)
     cbm = block_mask.to_c()
     ws_bytes = int(lib.flex_attn_fwd_workspace_bytes(DTYPES[q.dtype], B, Hq, Hkv, L, S, D, ctypes.byref(cbm)))
-    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _require_workspace(workspace, ws_bytes, dev)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     pages = flex_kv_pages()
     pages.page_table = page_table.data_ptr()
     pages.page_size, pages.max_pages, pages.num_pages = page_size, page_table.shape[1], num_pages

@@ -57,6 +57,25 @@ bool mask_implies_causal(const flex_mask_params* m) {
     return false;
 }
 
+// True when every row that sees a key also sees its own diagonal key j = p
+// (whenever p is a valid key): each clause of a PROGRAM holds a predicate that
+// is true at j = p (causal, window, chunk, stride or same document).  kv_lt and
+// head_lt are not: a clause made of them alone can hide the diagonal while
+// leaving far keys visible.
+bool mask_keeps_diagonal(const flex_mask_params* m) {
+    if (m->kind != FLEX_MASK_PROGRAM) return true;
+    for (int c = 0; c < m->n_clauses; ++c) {
+        bool has = false;
+        for (int l = 0; l < m->clause[c].n; ++l) {
+            const int k = m->clause[c].lit[l].kind;
+            has = has || k == FLEX_PRED_CAUSAL || k == FLEX_PRED_WINDOW || k == FLEX_PRED_CHUNK ||
+                  k == FLEX_PRED_STRIDE || k == FLEX_PRED_DOC;
+        }
+        if (!has) return false;
+    }
+    return true;
+}
+
 flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
     if (m->kind < FLEX_MASK_NOOP || m->kind > FLEX_MASK_PROGRAM)
         return fail(FLEX_ERR_PARAM, "unknown mask kind %d", m->kind);
@@ -381,15 +400,20 @@ static flex_status fwd_common(const void* q, const void* k, const void* v, int32
     a.kv_block = bm->kv_block;
     // Fixed softmax reference when the soft-cap bounds every visible score:
     // g < cap always, and a distance bias alpha*(kv - q) <= 0 under causal-type
-    // masks; rows then always keep their own (bias 0) key when q_offset + L <= S,
-    // so the range [ref - 120, ref + 64] (base 2) loses nothing.
+    // masks.  With the bias, a row's largest weight must also stay in range:
+    // that holds when every row that sees a key keeps its own (bias 0) key,
+    // which needs q_offset + L <= S and a mask whose every clause is true on
+    // the diagonal; the range [ref - 120, ref + 64] (base 2) then loses
+    // nothing.  A mask that can hide the diagonal while showing far keys (for
+    // example causal AND kv < 4) takes the moving reference instead.
     a.ref_mode = 0;
     a.ref_fixed = 0.0f;
     if (dtype == FLEX_BF16 && capped && max_scores == nullptr) {
         const double c2 = (double)score->cap * 1.4426950408889634;
         bool ok = c2 <= 92.0;
         if (score->kind == FLEX_SCORE_SOFTCAP_ALIBI)
-            ok = ok && mask_implies_causal(mask) && mask->q_offset + L <= S && !per_batch(mask);
+            ok = ok && mask_implies_causal(mask) && mask_keeps_diagonal(mask) && mask->q_offset + L <= S &&
+                 !per_batch(mask);
         if (ok) {
             a.ref_mode = 1;
             a.ref_fixed = (float)(c2 <= 63.0 ? c2 : 120.0 - c2);

@@ -7,6 +7,9 @@ from oracle import MaskMod, ScoreMod
 
 TOL_OUT = {"bf16": 2e-2, "f32": 1e-5}
 TOL_LSE = 1e-3
+# (what, out max-abs, lse max-abs) of every parity check of the session; the
+# session summary (conftest) prints the full-size ones and the worst case
+PARITY_LOG = []
 
 
 def require_gpu():
@@ -48,7 +51,9 @@ def assert_attention_close(out, lse, out_ref, lse_ref, dtype: str, what=""):
         fin = ~ref_inf
         lerr = np.abs(l[fin] - lse_ref[fin]).max() if fin.any() else 0.0
         print(f"[parity] {what}: out max-abs {err:.3e}, lse max-abs {lerr:.3e}")
+        PARITY_LOG.append((what, float(err), float(lerr)))
         assert lerr <= TOL_LSE, f"{what}: lse max-abs {lerr:.3e} > {TOL_LSE}"
     else:
         print(f"[parity] {what}: out max-abs {err:.3e}")
+        PARITY_LOG.append((what, float(err), None))
     return err

@@ -407,3 +407,28 @@ def test_per_batch_arrays_need_per_batch_block_mask(lib):
     b.mask.kv_lens = FAKE
     b.bm.B = b.bmq.B = b.B
     assert b.call(lib) == UNSUPPORTED                     # the backward takes none
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    """The binding checks every tensor it marshals (device, dtype, exact shape,
+    contiguity) and raises ValueError before a pointer reaches the library:
+    host tensors here, where no GPU exists, must never be passed on."""
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    bm = pbs.BlockMask(i32(1, 1, 1), i32(1, 1, 1, 1), i32(1, 1, 1), i32(1, 1, 1, 1), 64, 64, 64, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pbs.flex_attn_fwd(q, k, k, block_mask=bm)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pbs.flex_attn_fwd_paged(q, k, k, i32(1, 1), S=64, block_mask=bm)
+    with pytest.raises(ValueError):
+        pbs.flex_attn_bwd(q, k, k, q, q, torch.zeros((1, 2, 64)), block_mask=bm, block_mask_q=None)
+    with pytest.raises(ValueError, match="must be on"):
+        bm.to_c()
+    with pytest.raises(ValueError, match="must be on"):
+        pbs.flex_blockmask_build(pbs.MaskSpec(kind="causal"), 64, 64, 64, 64, out=bm)
+    # wrong shapes are caught whatever the device
+    bad = pbs.BlockMask(i32(1, 1, 2), i32(1, 1, 1, 1), i32(1, 1, 1), i32(1, 1, 1, 1), 64, 64, 64, 64)
+    with pytest.raises(ValueError, match="shape|must be on"):
+        bad._validate(torch.device("cpu"))

@@ -29,6 +29,7 @@ import torch
 import programmable_block_sparse_amd as pbs
 from gpu_common import require_gpu
 from oracle import MaskMod, ScoreMod, attention_backward, build_block_mask, transpose_block_mask
+from oracle import default_scale as oracle_default_scale
 from workloads import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, make_upstream
 from workloads.torch_io import specs, to_device
 
@@ -107,7 +108,7 @@ def run_bwd_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_k
     grads = pbs.flex_attn_bwd(qt, kt, vt, out, dot, lse, block_mask=bm, block_mask_q=bmq, score=sspec, mask=mspec,
                               scale=scale)
     torch.cuda.synchronize()
-    sc = pbs.default_scale(D) if scale is None else float(np.float32(scale))
+    sc = oracle_default_scale(D) if scale is None else float(np.float32(scale))
     ref = attention_backward(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), _widen(do, dtype), scale=sc,
                              score=smod, mask=mmod, q_offset=off)
     assert_grads_close(grads, ref, dtype, what)
@@ -250,7 +251,7 @@ def test_bwd_full_size_sampled(dev):
     for b, h in ((0, 0), (3, 15)):
         sl = lambda x: x[b:b + 1, h:h + 1]
         ref = attention_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(up["dout"]),
-                                 scale=pbs.default_scale(w.D), score=ScoreModAt(smod, h, w.Hq), mask=mmod,
+                                 scale=oracle_default_scale(w.D), score=ScoreModAt(smod, h, w.Hq), mask=mmod,
                                  q_offset=w.q_offset)
         got = tuple(x[b:b + 1, h:h + 1] for x in (dq, dk, dv))
         assert_grads_close(got, ref, "bf16", f"full size b={b} h={h}")
@@ -309,7 +310,7 @@ def test_bwd_full_size_d128(dev, name, pairs):
     mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"])
     smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
     print(f"[bwd parity] {name}: oracle over {len(pairs)} head(s)", flush=True)
-    ref_q, ref_k, ref_v = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=pbs.default_scale(w.D),
+    ref_q, ref_k, ref_v = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=oracle_default_scale(w.D),
                                              score=smod, mask=mmod, q_offset=w.q_offset, pairs=pairs, row_chunk=512)
     b = pairs[0][0]
     heads = [h for _, h in pairs]

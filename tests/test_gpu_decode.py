@@ -8,6 +8,7 @@ import torch
 import programmable_block_sparse_amd as pbs
 from gpu_common import assert_attention_close, assert_block_mask_equal, require_gpu
 from oracle import MaskMod, ScoreMod, attention, build_block_mask
+from oracle import default_scale as oracle_default_scale
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -71,7 +72,7 @@ def run(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, kind, window=0,
     else:
         out, lse = pbs.flex_attn_fwd(qt, _t(k, dtype, dev), _t(v, dtype, dev), block_mask=bm, score=sspec, mask=spec)
     torch.cuda.synchronize()
-    sc = pbs.default_scale(D)
+    sc = oracle_default_scale(D)
     out_ref, lse_ref = attention(_w(q, dtype), _w(k, dtype), _w(v, dtype), scale=sc, score=smod, mask=mod,
                                  q_offset=offs, kv_len=lens)
     assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)

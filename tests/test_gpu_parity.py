@@ -16,6 +16,7 @@ import torch
 import programmable_block_sparse_amd as pbs
 from gpu_common import TOL_LSE, assert_attention_close, assert_block_mask_equal, oracle_mods, require_gpu
 from oracle import MaskMod, ScoreMod, attention, build_block_mask
+from oracle import default_scale as oracle_default_scale
 from workloads import (EXTRA_WORKLOADS, WORKLOAD_ORDER, WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
                        workload_doc_ids)
 from workloads.torch_io import specs, to_device
@@ -153,7 +154,7 @@ def run_case(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_kind,
         out, lse = pbs.flex_attn_fwd(qt, kt, vt, block_mask=bm, score=sspec, mask=mspec, scale=scale,
                                      return_lse=with_lse)
     torch.cuda.synchronize()
-    sc = pbs.default_scale(D) if scale is None else float(np.float32(scale))
+    sc = oracle_default_scale(D) if scale is None else float(np.float32(scale))
     out_ref, lse_ref, mx_ref = attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale=sc,
                                          score=smod, mask=mmod, q_offset=off, with_max=True)
     err = assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
@@ -227,7 +228,7 @@ def test_packed_documents_launch_order(dev, D, qb, L):
                                  block_mask=bm, mask=mspec)
     torch.cuda.synchronize()
     out_ref, lse_ref, _ = attention(_widen(q, "bf16"), _widen(k, "bf16"), _widen(v, "bf16"),
-                                    scale=pbs.default_scale(D), score=ScoreMod("none"), mask=mmod, q_offset=0,
+                                    scale=oracle_default_scale(D), score=ScoreMod("none"), mask=mmod, q_offset=0,
                                     with_max=True)
     assert_attention_close(out, lse, out_ref, lse_ref, "bf16", f"packed documents D={D} qb={qb}")
 
@@ -282,7 +283,7 @@ def test_softcap_tiers_by_score_magnitude(dev, mask_kind, score):
     out, lse = pbs.flex_attn_fwd(_tensor(q, "bf16", dev), _tensor(k, "bf16", dev), _tensor(v, "bf16", dev),
                                  block_mask=bm, score=pbs.ScoreSpec(**score), mask=mspec)
     torch.cuda.synchronize()
-    out_ref, lse_ref = attention(_widen(q, "bf16"), _widen(k, "bf16"), _widen(v, "bf16"), scale=pbs.default_scale(D),
+    out_ref, lse_ref = attention(_widen(q, "bf16"), _widen(k, "bf16"), _widen(v, "bf16"), scale=oracle_default_scale(D),
                                  score=ScoreMod(**score), mask=mmod, q_offset=0)
     assert_attention_close(out, lse, out_ref, lse_ref, "bf16", f"tiers {score} {mask_kind}")
 
@@ -363,13 +364,81 @@ def test_workload_parity_sampled(dev, name):
         bs = sorted({0, w.B - 1})
         hs = sorted({0, w.Hq - 1, int(rng.integers(0, w.Hq))})
         rows = _sample_rows(w, rng)
-    out_ref, lse_ref = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod,
+    out_ref, lse_ref = attention(inp["q"], inp["k"], inp["v"], scale=oracle_default_scale(w.D), score=smod,
                                  mask=mmod, q_offset=w.q_offset, rows=rows, heads=hs, batches=bs)
     got_o = out_np[np.ix_(list(bs), list(hs), rows)]
     got_l = lse_np[np.ix_(list(bs), list(hs), rows)]
     assert_attention_close(got_o, got_l, out_ref, lse_ref, w.dtype, name)
     # properties that hold at any size: finite everywhere rows see keys, no NaN
     assert not np.isnan(out_np).any() and not np.isnan(lse_np).any()
+
+
+# Whole (batch, head) slices at full size: every row of the first slice and
+# of the last batch's last query head (plus one slice between them), so the
+# launch orders that only change behaviour at full size (longest document
+# first, the XCD-grouped GQA head order, the highest Q block first) are
+# checked end to end on every row they touch.  The decode / verify workload
+# is small enough per row to check every output.
+FULL_SLICE_WORKLOADS = ["causal_softcap_alibi", "doc_causal", "window_sinks_gqa", "decode_verify",
+                        "prefix_lm_alibi", "chunked_gqa"]
+
+
+@pytest.mark.parametrize("name", FULL_SLICE_WORKLOADS)
+def test_workload_parity_full_slices(dev, name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    q, k, v, doc_t = to_device(w, inp, dev)
+    mspec, sspec = specs(w, doc_t)
+    bm = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
+    out, lse = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    torch.cuda.synchronize()
+    out_np = out.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    del q, k, v, out, lse
+    mmod, smod = oracle_mods(w, inp["doc_id"])
+    if w.L * w.S <= 1 << 20:
+        slices = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    else:
+        mid = (w.B // 2, (w.Hq // 2) + 1 if w.Hq > 2 else 0)
+        slices = sorted({(0, 0), mid, (w.B - 1, w.Hq - 1)})
+    worst_o = worst_l = 0.0
+    for b, h in slices:
+        out_ref, lse_ref = attention(inp["q"], inp["k"], inp["v"], scale=oracle_default_scale(w.D), score=smod,
+                                     mask=mmod, q_offset=w.q_offset, heads=[h], batches=[b])
+        err_o = assert_attention_close(out_np[b:b + 1, h:h + 1], lse_np[b:b + 1, h:h + 1], out_ref, lse_ref,
+                                       w.dtype, f"{name} full slice b={b} h={h}")
+        fin = np.isfinite(lse_ref)
+        err_l = float(np.abs(lse_np[b:b + 1, h:h + 1][fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+        worst_o, worst_l = max(worst_o, err_o), max(worst_l, err_l)
+    print(f"[parity] {name}: {len(slices)} full (batch, head) slices of {w.L} rows, worst out max-abs "
+          f"{worst_o:.3e}, worst lse max-abs {worst_l:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,D,L,S,qb", [("bf16", 64, 300, 300, 128), ("bf16", 128, 300, 300, 128),
+                                            ("f32", 64, 300, 300, 64), ("f32", 128, 200, 200, 64),
+                                            ("bf16", 128, 16, 3000, 16)])
+def test_default_scale_is_the_pages_value(dev, dtype, D, L, S, qb):
+    """scale=None (the library's default, scale <= 0 at the C ABI) gives
+    bit-for-bit the result of passing the pages' default 1/sqrt(D), computed
+    here in float64 and rounded once to float32 (2kiu guide, section 6.2),
+    on the prefill and the split-KV decode paths."""
+    rng = np.random.default_rng(77 + D + L)
+    Hq, Hkv = 4, 2
+    x = [rng.standard_normal(s, dtype=np.float32) for s in ((1, Hq, L, D), (1, Hkv, S, D), (1, Hkv, S, D))]
+    q, k, v = (_tensor(t, dtype, dev) for t in x)
+    mspec = pbs.MaskSpec(kind="causal")
+    sspec = pbs.ScoreSpec(kind="softcap", cap=30.0)
+    bm = pbs.flex_blockmask_build(mspec, L, S, qb, 64, device=dev)
+    o_def, l_def = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec)
+    o_exp, l_exp = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec, scale=oracle_default_scale(D))
+    torch.cuda.synchronize()
+    assert torch.equal(o_def, o_exp) and torch.equal(l_def, l_exp), \
+        f"default scale differs from float32(1/sqrt({D})) = {oracle_default_scale(D)!r}"
+    # and a different scale does change the result (the argument is not ignored)
+    o_oth, _ = pbs.flex_attn_fwd(q, k, v, block_mask=bm, score=sspec, mask=mspec,
+                                 scale=oracle_default_scale(D) * 1.25)
+    torch.cuda.synchronize()
+    assert not torch.equal(o_def, o_oth)
 
 
 def test_run_to_run_bitwise_determinism(dev):
@@ -450,6 +519,23 @@ def test_attention_program_masks(dev, dtype, D):
                  what=f"{dtype} D={D} {name} {score}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_softcap_alibi_programs_that_hide_the_diagonal(dev, D):
+    """Soft-cap plus distance bias under mask programs with a causal clause
+    and a clause that can hide a row's own key, (causal) AND (kv < 4) and
+    (causal) AND (h < 8 OR kv < 4): rows far down see only distant keys whose
+    biased scores sit far below the cap, so their weights must not underflow
+    (each such row has a finite lse).  Long enough rows that the bias of the
+    nearest visible key reaches hundreds (base 2) in the first heads."""
+    programs = {"causal_and_kv_lt": ((("causal", 0),), (("kv_lt", 4),)),
+                "causal_and_head_or_kv": ((("causal", 0),), (("head_lt", 8), ("kv_lt", 4)))}
+    for i, (name, clauses) in enumerate(programs.items()):
+        bm_heads = 16 if name == "causal_and_head_or_kv" else 1
+        run_case(dev, seed=820 + i + D, dtype="bf16", B=1, Hq=16, Hkv=16 if D == 64 else 4, L=1024, S=1024, D=D,
+                 qb=128, kb=64, score=dict(kind="softcap_alibi", cap=30.0, alibi_m=8.0), mask_kind="program",
+                 clauses=clauses, bm_heads=bm_heads, what=f"softcap_alibi D={D} {name}")
+
+
 @pytest.mark.parametrize("case", ["softcap_alibi_causal", "none_noop", "softcap_doc", "alibi_program", "max_window"])
 def test_attention_128_row_workgroups_d64(dev, case):
     """bf16 at head dim 64 with B*Hq*ceil(L/128) >= 768 row blocks, enough
@@ -505,3 +591,50 @@ def test_decode_path_programs_alibi_and_max(dev):
             assert pbs.flex_attn_fwd_workspace_bytes(torch.bfloat16, B, G * Hkv, Hkv, L, S, D, probe) > 0
             run_case(dev, seed=800 + i + D, dtype="bf16", B=B, Hq=G * Hkv, Hkv=Hkv, L=L, S=S, D=D, qb=qb, kb=64,
                      score=score, with_max=with_max, what=f"decode D={D} {mask} {score} max={with_max}", **mask)
+
+
+def test_binding_rejects_wrong_buffers(dev):
+    """Every tensor handed to the binding is checked (device, dtype, exact
+    shape, contiguity) before any pointer is marshalled: each wrong buffer is
+    a ValueError and the output the call would have written is untouched."""
+    rng = np.random.default_rng(5)
+    B, H, L, D = 1, 2, 130, 64
+    x = [_tensor(rng.standard_normal((B, H, L, D), dtype=np.float32), "bf16", dev) for _ in range(3)]
+    q, k, v = x
+    mspec = pbs.MaskSpec(kind="causal")
+    bm = pbs.flex_blockmask_build(mspec, L, L, 128, 64, device=dev)
+    good_out = torch.full((B, H, L, D), 7.0, dtype=torch.bfloat16, device=dev)
+    cases = {
+        "out too small": dict(out=torch.empty((B, H, L - 1, D), dtype=torch.bfloat16, device=dev)),
+        "out wrong dtype": dict(out=torch.empty((B, H, L, D), dtype=torch.float32, device=dev)),
+        "out strided": dict(out=torch.empty((B, H, D, L), dtype=torch.bfloat16, device=dev).transpose(2, 3)),
+        "out on host": dict(out=torch.empty((B, H, L, D), dtype=torch.bfloat16)),
+        "lse wrong dtype": dict(out=good_out, lse=torch.empty((B, H, L), dtype=torch.bfloat16, device=dev)),
+        "lse too small": dict(out=good_out, lse=torch.empty((B, H, L - 5), dtype=torch.float32, device=dev)),
+    }
+    for what, kw in cases.items():
+        with pytest.raises(ValueError):
+            pbs.flex_attn_fwd(q, k, v, block_mask=bm, mask=mspec, **kw)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pbs.flex_attn_fwd(q, k.cpu(), v, block_mask=bm, mask=mspec, out=good_out)
+    bm64 = pbs.BlockMask(bm.kv_num_blocks.long(), bm.kv_indices, bm.full_kv_num_blocks, bm.full_kv_indices,
+                         bm.q_block, bm.kv_block, bm.L, bm.S)
+    with pytest.raises(ValueError):
+        pbs.flex_attn_fwd(q, k, v, block_mask=bm64, mask=mspec, out=good_out)
+    short = pbs.BlockMask(bm.kv_num_blocks, bm.kv_indices[..., :1].contiguous(), bm.full_kv_num_blocks,
+                          bm.full_kv_indices, bm.q_block, bm.kv_block, bm.L, bm.S)
+    with pytest.raises(ValueError):
+        pbs.flex_attn_fwd(q, k, v, block_mask=short, mask=mspec, out=good_out)
+    # the split-KV path's workspace: a too-small one is refused, not replaced
+    Lq, S = 16, 3000
+    qd = _tensor(rng.standard_normal((1, 4, Lq, D), dtype=np.float32), "bf16", dev)
+    kd = _tensor(rng.standard_normal((1, 1, S, D), dtype=np.float32), "bf16", dev)
+    mdec = pbs.MaskSpec(kind="causal")
+    bmd = pbs.flex_blockmask_build(mdec, Lq, S, 16, 64, device=dev)
+    need = pbs.flex_attn_fwd_workspace_bytes(torch.bfloat16, 1, 4, 1, Lq, S, D, bmd)
+    assert need > 0
+    with pytest.raises(ValueError, match="workspace"):
+        pbs.flex_attn_fwd(qd, kd, kd, block_mask=bmd, mask=mdec,
+                          workspace=torch.empty(need - 16, dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    assert bool((good_out == 7.0).all()), "a rejected call wrote its output"

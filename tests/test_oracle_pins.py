@@ -153,6 +153,29 @@ def test_matches_sdpa_noop_and_causal(B, H, L, S, D):
     assert np.abs(out - ref.numpy()).max() < 1e-12
 
 
+@pytest.mark.parametrize("D", [1, 2, 3, 4, 5, 16, 64, 96, 128, 256])
+def test_default_scale_is_one_over_sqrt_d_in_float32(D):
+    """The default scale (2kiu guide, section 6.2: 1/sqrt(E), E the embedding
+    dimension) as the float32 value handed to the kernel: the float32 nearest
+    to 1/sqrt(D).  Exact for squares of powers of two; otherwise s is within
+    half an ulp of 1/sqrt(D), checked through s^2 * D = 1 to first order, and
+    torch's SDPA with its own default scale matches the oracle run with it."""
+    from oracle import default_scale
+    s = default_scale(D)
+    assert np.float32(s) == s
+    exact = 1.0 / math.sqrt(D)
+    assert abs(s - exact) <= np.spacing(np.float32(exact)) / 2
+    if D in (1, 4, 16, 64, 256):
+        assert s == {1: 1.0, 4: 0.5, 16: 0.25, 64: 0.125, 256: 0.0625}[D]
+    assert abs(s * s * D - 1.0) <= 2 * 2.0 ** -24
+    g = torch.Generator().manual_seed(D)
+    q, k, v = (torch.randn(1, 1, 9, D, generator=g, dtype=torch.float64) for _ in range(3))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).numpy()
+    out, _ = attention(q.numpy(), k.numpy(), v.numpy(), scale=s, score=ScoreMod(), mask=MaskMod(), q_offset=0)
+    # the float32 rounding of the scale moves the result by at most ~1e-7 relative
+    assert np.abs(out - ref).max() < 1e-6
+
+
 def test_lse_matches_torch_logsumexp():
     g = torch.Generator().manual_seed(5)
     q = torch.randn(1, 2, 9, 8, generator=g, dtype=torch.float64)
