@@ -221,55 +221,28 @@ def main():
         build_only()
         attend(bm_step)
 
-    def timed(fn, n):
-        stream = torch.cuda.current_stream(dev)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(n):
-            fn()
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / n
-
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    mode = "eager"
     runners = {"step": step, "fwd": fwd, "mask": build_only}
+    mode = "eager"
     if not args.eager:
-        # One HIP graph per measured unit, replayed back to back.  Each replay is
-        # checked against the eager result (the graph holds only our kernels).
-        out_ref, lse_ref = out.clone(), lse.clone()
-        graphs = {}
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            for name, fn in runners.items():
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    fn()
-                graphs[name] = g
-        torch.cuda.current_stream(dev).wait_stream(side)
-        torch.cuda.synchronize()
-        for i in range(3):
-            out.zero_()
-            lse.zero_()
-            graphs["step"].replay()
-            torch.cuda.synchronize()
-            if not (torch.equal(out, out_ref) and torch.equal(lse, lse_ref)):
-                raise RuntimeError(f"graph replay {i} differs from the eager result")
-            step()                       # eager work between replays
-            torch.cuda.synchronize()
-        runners = {name: g.replay for name, g in graphs.items()}
+        runners = graph_runners(runners, dev, ([out, lse], step))
         mode = "hip_graph"
-    ms_step = timed(runners["step"], args.steps)
-    ms_fwd = timed(runners["fwd"], args.steps)
-    ms_mask = timed(runners["mask"], args.steps)
-    print(f"bench: step {ms_step * 1e3:.1f} us, fwd {ms_fwd * 1e3:.1f} us, block mask {ms_mask * 1e3:.1f} us "
-          f"({mode})", file=sys.stderr, flush=True)
+    tm = time_units(runners, args, dev)
+    ms_step, ms_fwd, ms_mask = tm["ms_per_step"], tm["fwd"]["median_ms"], tm["mask"]["median_ms"]
+    print(f"bench: step {ms_step * 1e3:.1f} us ({args.steps} steps; windows median "
+          f"{tm['step']['median_ms'] * 1e3:.1f} us), fwd {ms_fwd * 1e3:.1f} us "
+          f"[{tm['fwd']['min_ms'] * 1e3:.1f}, {tm['fwd']['max_ms'] * 1e3:.1f}], "
+          f"block mask {ms_mask * 1e3:.1f} us ({mode}, {tm['calls_per_window']} calls per window, "
+          f"{tm['windows']} windows)", file=sys.stderr, flush=True)
 
+    # a step holds the forward plus the BlockMask build, so it cannot be faster
+    tm["step_ge_fwd"] = bool(tm["step"]["median_ms"] >= ms_fwd)
+    if not tm["step_ge_fwd"]:
+        print(f"bench: WARNING step median {tm['step']['median_ms'] * 1e3:.1f} us below fwd median "
+              f"{ms_fwd * 1e3:.1f} us: timing unreliable on this run", file=sys.stderr, flush=True)
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (ms_fwd * 1e-3) / 1e12
     if w.name == "decode_verify":
@@ -295,7 +268,7 @@ def main():
                    "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset,
                    "doc_lengths": inp["doc_lengths"], "page_size": args.paged or None},
         "roofline": roof,
-        "fwd_ms": ms_fwd, "blockmask_ms": ms_mask, "launch_mode": mode,
+        "fwd_ms": ms_fwd, "blockmask_ms": ms_mask, "launch_mode": mode, "timing": tm,
         "fwd_tflops_visited": fwd_tflops, "pct_bf16_peak_fwd": 100.0 * fwd_tflops / BF16_PEAK_TFLOPS,
         "visited_block_flops": flops, "algorithmic_bytes": alg_bytes,
         "hbm_gbs_fwd": alg_bytes / (ms_fwd * 1e-3) / 1e9,
@@ -305,34 +278,109 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+# Calls of one unit captured back to back in one HIP graph: a replay then
+# costs one graph launch per GRAPH_CALLS calls, so the launch overhead of a
+# replay (about 10 us on this stack, as long as a BlockMask build) does not
+# count as kernel time.
+GRAPH_CALLS = 10
+
+
+class GraphUnit:
+    """A unit of work replayed from HIP graphs: ``run(n)`` enqueues n calls
+    (n // GRAPH_CALLS replays of the multi-call graph, then single-call ones)."""
+
+    def __init__(self, g1, gn):
+        self.g1, self.gn = g1, gn
+
+    def run(self, n):
+        for _ in range(n // GRAPH_CALLS):
+            self.gn.replay()
+        for _ in range(n % GRAPH_CALLS):
+            self.g1.replay()
+
+
+class EagerUnit:
+    def __init__(self, fn):
+        self.fn = fn
+
+    def run(self, n):
+        for _ in range(n):
+            self.fn()
+
+
 def graph_runners(runners, dev, check):
-    """Capture each runner in its own HIP graph (on a side stream) and check
-    three replays of ``check``'s graph against the eager result, with eager work
-    between them.  Returns name -> replay."""
+    """Capture each runner in HIP graphs of one call and of GRAPH_CALLS calls
+    (on a side stream) and check three replays of ``check``'s one-call graph,
+    then three of its multi-call graph, against the eager result, with eager
+    work between them.  Returns name -> GraphUnit."""
     import torch
     graphs = {}
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
         for name, fn in runners.items():
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                fn()
-            graphs[name] = g
+            pair = []
+            for calls in (1, GRAPH_CALLS):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for _ in range(calls):
+                        fn()
+                pair.append(g)
+            graphs[name] = GraphUnit(*pair)
     torch.cuda.current_stream(dev).wait_stream(side)
     torch.cuda.synchronize()
     bufs, eager = check
     ref = [b.clone() for b in bufs]
-    for i in range(3):
+    first = graphs[next(iter(graphs))]
+    for i, g in enumerate([first.g1] * 3 + [first.gn] * 3):
         for b in bufs:
             b.zero_()
-        graphs[next(iter(graphs))].replay()
+        g.replay()
         torch.cuda.synchronize()
         if not all(torch.equal(b, r) for b, r in zip(bufs, ref)):
             raise RuntimeError(f"graph replay {i} differs from the eager result")
         eager()
         torch.cuda.synchronize()
-    return {name: g.replay for name, g in graphs.items()}
+    return graphs
+
+
+def time_units(units, args, dev, windows=5, min_calls=50, warm_ms=100.0):
+    """Time every unit on the stream its kernels run on (HIP events).
+
+    First the step unit runs until at least ``warm_ms`` of GPU time has passed
+    (clocks and caches settle).  Then ``ms_per_step`` is the time of exactly
+    ``args.steps`` steps, and each unit is timed in ``windows`` interleaved
+    windows of max(min_calls, args.steps) calls: median, min and max per call.
+    Units are GraphUnit or EagerUnit (name -> unit); plain callables are
+    wrapped as eager units."""
+    import torch
+    units = {n: (u if hasattr(u, "run") else EagerUnit(u)) for n, u in units.items()}
+    stream = torch.cuda.current_stream(dev)
+
+    def window(unit, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        unit.run(n)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    warm, warm_calls = 0.0, 0
+    while warm < warm_ms:
+        warm += window(units["step"], 20)
+        warm_calls += 20
+    ms_per_step = window(units["step"], args.steps) / args.steps
+    n = max(min_calls, args.steps)
+    per = {name: [] for name in units}
+    for _ in range(windows):
+        for name, unit in units.items():
+            per[name].append(window(unit, n) / n)
+    out = {"ms_per_step": ms_per_step, "warmup_ms": warm, "warmup_calls": warm_calls, "windows": windows,
+           "calls_per_window": n, "graph_calls": GRAPH_CALLS}
+    for name, xs in per.items():
+        out[name] = {"median_ms": float(np.median(xs)), "min_ms": float(min(xs)), "max_ms": float(max(xs))}
+    return out
 
 
 def bwd_kernel_names(w) -> str:
@@ -401,17 +449,6 @@ def main_bwd(args):
     def transpose_only():
         pbs.flex_blockmask_transpose(bm_step, out=bmq_step)
 
-    def timed(fn, n):
-        stream = torch.cuda.current_stream(dev)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(n):
-            fn()
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / n
-
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -421,10 +458,10 @@ def main_bwd(args):
     if not args.eager:
         runners = graph_runners(runners, dev, ([out, lse, dq, dk, dv], step))
         mode = "hip_graph"
-    ms_step = timed(runners["step"], args.steps)
-    ms_bwd = timed(runners["bwd"], args.steps)
-    ms_tr = timed(runners["transpose"], args.steps)
-    print(f"bench: step {ms_step * 1e3:.1f} us, bwd {ms_bwd * 1e3:.1f} us, transpose {ms_tr * 1e3:.1f} us "
+    tm = time_units(runners, args, dev)
+    ms_step, ms_bwd, ms_tr = tm["ms_per_step"], tm["bwd"]["median_ms"], tm["transpose"]["median_ms"]
+    print(f"bench: step {ms_step * 1e3:.1f} us, bwd {ms_bwd * 1e3:.1f} us "
+          f"[{tm['bwd']['min_ms'] * 1e3:.1f}, {tm['bwd']['max_ms'] * 1e3:.1f}], transpose {ms_tr * 1e3:.1f} us "
           f"({mode})", file=sys.stderr, flush=True)
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     bwd_tflops = bwd_flops / (ms_bwd * 1e-3) / 1e12
@@ -440,7 +477,7 @@ def main_bwd(args):
         "config": {"workload": w.name + "_train", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S,
                    "D": w.D, "mask": w.mask, "score": w.score, "cap": w.cap, "window": w.window,
                    "sinks": w.sinks, "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset},
-        "roofline": roof, "bwd_ms": ms_bwd, "transpose_ms": ms_tr, "launch_mode": mode,
+        "roofline": roof, "bwd_ms": ms_bwd, "transpose_ms": ms_tr, "launch_mode": mode, "timing": tm,
         "bwd_tflops_visited": bwd_tflops, "fwd_visited_flops": fwd_flops, "bwd_visited_flops": bwd_flops,
     }
     if not args.no_cpu_baseline:
@@ -452,22 +489,16 @@ def cpu_baseline_bwd(args, w, inp, up, grads, flops):
     """Time the float64 backward oracle on (batch, head) slices of the workload
     (about 10 s) and compare the GPU gradients of those slices."""
     from oracle import MaskMod, ScoreMod, attention_backward
-    import programmable_block_sparse_amd as pbs
+    from oracle import default_scale as oracle_default_scale
 
-    cores = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = None
+    cores, cpu_model, blas_threads = host_info()
     mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"], clauses=w.clauses)
     smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
-    group = w.Hq // w.Hkv
     pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     sample, t_total, refs = [], 0.0, {}
     for (b, h) in pairs:
         t0 = time.perf_counter()
-        refs[(b, h)] = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=pbs.default_scale(w.D),
+        refs[(b, h)] = attention_backward(inp["q"], inp["k"], inp["v"], up["dout"], scale=oracle_default_scale(w.D),
                                           score=smod, mask=mmod, q_offset=w.q_offset, pairs=[(b, h)])
         t_total += time.perf_counter() - t0
         sample.append((b, h))
@@ -477,28 +508,48 @@ def cpu_baseline_bwd(args, w, inp, up, grads, flops):
     dq = grads[0].float().cpu().numpy()
     # dq of a sampled head is complete; dk, dv of a K/V head need all its query heads
     err_dq = max(float(np.abs(dq[b, h] - refs[(b, h)][0][b, h]).max()) for (b, h) in sample)
+    dense_per_head = 12 * w.D * w.L * w.S      # S, O = PV, dP, dV, dK, dQ over every (row, key) pair
     return {
-        "cpu_baseline": {"value": flops / (w.B * w.Hq) * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
+        "cpu_baseline": {"value": dense_per_head * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
                          "cores": blas_threads or cores, "kind": "oracle",
+                         "flops_counted": "dense: 12*D*L*S per (batch, head) slice, as the oracle computes",
                          "sample": f"{len(sample)} of {w.B * w.Hq} (batch, head) slices, all rows; float64 dense "
-                                   f"backward oracle, {t_total:.1f} s; host cores {cores}"},
+                                   f"backward oracle, {t_total:.1f} s; host cores {cores}, BLAS threads "
+                                   f"{blas_threads}, CPU {cpu_model}",
+                         "host_cores": cores, "blas_threads": blas_threads, "cpu_model": cpu_model},
         "parity_on_bench_buffers": {"dq_max_abs": err_dq, "heads_checked": len(sample)},
     }
 
 
-def cpu_baseline(args, w, inp, out, lse, flops):
-    """Time the float64 oracle on whole (batch, head) slices of the workload and
-    compare the GPU output on those rows."""
-    import torch
-    from oracle import MaskMod, ScoreMod, attention, build_block_mask
-    import programmable_block_sparse_amd as pbs
-
+def host_info():
+    """Cores this process may run on, the CPU model and the BLAS thread count."""
     cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        blas_threads = None
+        blas = None
+    return cores, model, blas
+
+
+def cpu_baseline(args, w, inp, out, lse, flops):
+    """Time the float64 oracle on whole (batch, head) slices of the workload and
+    compare the GPU output on those rows.  The oracle forms every score of a
+    row (dense), so its rate is counted on the dense FLOPs it performs:
+    4*D*L*S per (batch, head) slice (QK^T and PV)."""
+    from oracle import MaskMod, ScoreMod, attention, build_block_mask
+    from oracle import default_scale as oracle_default_scale
+
+    cores, cpu_model, blas_threads = host_info()
     mmod = MaskMod(w.mask, window=w.window, sinks=w.sinks, doc_id=inp["doc_id"], clauses=w.clauses)
     smod = ScoreMod(w.score, cap=w.cap, alibi_m=w.alibi_m)
     t0 = time.perf_counter()
@@ -506,19 +557,22 @@ def cpu_baseline(args, w, inp, out, lse, flops):
     visible = int(ref_bm["counts"].sum())
     t_bm = time.perf_counter() - t0
     heads_total = w.B * w.Hq
-    per_head_flops = flops / heads_total
-    # about 10 s of work: calibrate on one head, then run the rest of the sample
+    dense_per_head = 4 * w.D * w.L * w.S
+    # about 10 s of work: calibrate on one head, then run the rest of the sample;
+    # the last batch's last head is always in the sample
     pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     t0 = time.perf_counter()
-    o1, l1 = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod, mask=mmod,
+    o1, l1 = attention(inp["q"], inp["k"], inp["v"], scale=oracle_default_scale(w.D), score=smod, mask=mmod,
                        q_offset=w.q_offset, heads=[0], batches=[0])
     t_one = time.perf_counter() - t0
-    n = args.cpu_sample_heads or int(max(1, min(len(pairs), 10.0 // max(t_one, 1e-3))))
-    sample = pairs[:n]
+    n = args.cpu_sample_heads or int(max(2, min(len(pairs), 10.0 // max(t_one, 1e-3))))
+    sample = pairs[:max(1, n - 1)]
+    if pairs[-1] not in sample:
+        sample.append(pairs[-1])
     outs = {(0, 0): (o1, l1)}
     t0 = time.perf_counter()
     for (b, h) in sample[1:]:
-        outs[(b, h)] = attention(inp["q"], inp["k"], inp["v"], scale=pbs.default_scale(w.D), score=smod,
+        outs[(b, h)] = attention(inp["q"], inp["k"], inp["v"], scale=oracle_default_scale(w.D), score=smod,
                                  mask=mmod, q_offset=w.q_offset, heads=[h], batches=[b])
     t_rest = time.perf_counter() - t0
     t_total = t_one + t_rest
@@ -528,14 +582,26 @@ def cpu_baseline(args, w, inp, out, lse, flops):
     fin = [np.isfinite(outs[(b, h)][1][0, 0]) for (b, h) in sample]
     err_l = max(float(np.abs(lse_np[b, h][f] - outs[(b, h)][1][0, 0][f]).max()) if f.any() else 0.0
                 for (b, h), f in zip(sample, fin))
+    inf_ok = all(np.array_equal(np.isneginf(lse_np[b, h]), ~f) for (b, h), f in zip(sample, fin))
+    tol_out = 2e-2 if w.dtype == "bf16" else 1e-5
+    within = bool(err_o <= tol_out and err_l <= 1e-3 and inf_ok)
+    if not within:
+        print(f"bench: PARITY FAILURE on the bench buffers: out {err_o:.3e} (tol {tol_out}), lse {err_l:.3e} "
+              f"(tol 1e-3), -inf pattern {'ok' if inf_ok else 'differs'}", file=sys.stderr, flush=True)
     return {
-        "cpu_baseline": {"value": per_head_flops * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
+        "cpu_baseline": {"value": dense_per_head * len(sample) / t_total / 1e12, "unit": "TFLOP/s",
                          "cores": blas_threads or cores, "kind": "oracle",
+                         "flops_counted": "dense: 4*D*L*S per (batch, head) slice, as the oracle computes",
                          "sample": f"{len(sample)} of {heads_total} (batch, head) slices, all {w.L} rows each; "
-                                   f"float64 dense oracle, {t_total:.1f} s; host cores {cores}"},
+                                   f"float64 dense oracle, {t_total:.1f} s; host cores {cores}, "
+                                   f"BLAS threads {blas_threads}, CPU {cpu_model}",
+                         "host_cores": cores, "blas_threads": blas_threads, "cpu_model": cpu_model,
+                         "seconds": t_total},
         "cpu_blockmask_oracle_s": t_bm,
         "visible_element_flops": 4 * w.D * visible * w.B * w.Hq,
-        "parity_on_bench_buffers": {"out_max_abs": err_o, "lse_max_abs": err_l, "rows_checked": len(sample) * w.L},
+        "parity_on_bench_buffers": {"out_max_abs": err_o, "lse_max_abs": err_l, "neg_inf_pattern_equal": inf_ok,
+                                    "rows_checked": len(sample) * w.L, "slices": [list(p) for p in sample],
+                                    "tolerance": {"out": tol_out, "lse": 1e-3}, "within_tolerance": within},
     }
 
 
