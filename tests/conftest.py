@@ -25,9 +25,14 @@ def pytest_terminal_summary(terminalreporter):
         return
     tr = terminalreporter
     tr.section("parity max errors (GPU vs CPU oracle)")
+    full = {}
     for what, eo, el in PARITY_LOG:
         if "full slice" in what:
-            tr.write_line(f"{what}: out {eo:.3e}" + ("" if el is None else f", lse {el:.3e}"))
+            name = what.split(" full slice")[0]
+            n, o, l = full.get(name, (0, 0.0, 0.0))
+            full[name] = (n + 1, max(o, eo), max(l, el or 0.0))
+    for name, (n, o, l) in full.items():
+        tr.write_line(f"{name}: {n} full (batch, head) slices, out max-abs {o:.3e}, lse max-abs {l:.3e}")
     worst_o = max(PARITY_LOG, key=lambda r: r[1])
     with_l = [r for r in PARITY_LOG if r[2] is not None]
     tr.write_line(f"{len(PARITY_LOG)} checks; worst out {worst_o[1]:.3e} ({worst_o[0]})")
