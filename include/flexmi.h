@@ -430,6 +430,30 @@ flex_status flex_attn_fwd_paged(const void* q, const void* k, const void* v, int
                                 const flex_block_mask* bm, const flex_kv_pages* pages, void* out, float* lse,
                                 float* max_scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch array behind flex_attn_fwd_noalloc (per GPU). */
+#define FLEX_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* flex_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the split-KV decode partials that flex_attn_fwd keeps
+ * in the caller's workspace go to a file-scope device array of
+ * FLEX_NOALLOC_SCRATCH_BYTES inside the library instead (one per GPU, held
+ * until the process ends; set up on the first call on each device).  The call
+ * allocates nothing and frees nothing.  Every argument is as for
+ * flex_attn_fwd; inputs and outputs are still the caller's.
+ * All calls on one GPU share its array: calls that overlap in time on that
+ * GPU (different streams, or threads without ordering) race and must not be
+ * issued.  Calls queued in order on one stream are safe.
+ * Errors: as flex_attn_fwd; WORKSPACE when the call would need more than
+ * FLEX_NOALLOC_SCRATCH_BYTES of scratch (flex_attn_fwd_workspace_bytes
+ * gives the need); HIP when the array's device address cannot be found. */
+flex_status flex_attn_fwd_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D,
+                                  const int64_t q_strides[3], const int64_t k_strides[3],
+                                  const int64_t v_strides[3], float scale,
+                                  const flex_score_params* score, const flex_mask_params* mask,
+                                  const flex_block_mask* bm, void* out, float* lse, void* stream);
+
 /* Static name of a status code. */
 const char* flex_status_string(int32_t status);
 

@@ -34,7 +34,7 @@ __all__ = [
     "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
     "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_aux", "flex_attn_fwd_workspace_bytes",
     "BlockMaskQ", "flex_blockmask_transpose", "flex_attn_bwd", "flex_attn_bwd_workspace_bytes",
-    "flex_attn_fwd_paged",
+    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc",
     "flex_status_string", "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "PREDICATES", "EXPORTED_SYMBOLS",
 ]
 
@@ -46,7 +46,7 @@ MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
                     "flex_blockmask_transpose", "flex_attn_bwd_workspace_bytes", "flex_attn_bwd",
-                    "flex_attn_fwd_paged",
+                    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc",
                     "flex_blockmask_to_dense", "flex_blockmask_grid", "flex_blockmask_sparsity",
                     "flex_blockmask_slice", "flex_blockmask_adjust",
                     "flex_status_string", "flex_last_error")
@@ -128,6 +128,10 @@ def load_library():
                                         ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask),
                                         ctypes.POINTER(flex_kv_pages), P, P, P, P, ctypes.c_size_t, P]
     lib.flex_attn_fwd_paged.restype = ctypes.c_int
+    lib.flex_attn_fwd_noalloc.argtypes = [P, P, P, I32, I32, I32, I32, I64, I64, I32, I64x3, I64x3, I64x3,
+                                          ctypes.c_float, ctypes.POINTER(flex_score_params),
+                                          ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask), P, P, P]
+    lib.flex_attn_fwd_noalloc.restype = ctypes.c_int
     lib.flex_blockmask_transpose.argtypes = [ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P]
     lib.flex_blockmask_transpose.restype = ctypes.c_int
     lib.flex_attn_bwd_workspace_bytes.argtypes = [I32, I32, I32, I32, I64, I64, I32, ctypes.POINTER(flex_block_mask)]
@@ -497,6 +501,43 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_ma
     ``return_lse`` is false.  ``scale=None`` selects 1/sqrt(D).
     """
     out, lse, _ = _fwd(q, k, v, block_mask, score, mask, scale, return_lse, False, out, lse, None, workspace)
+    return out, lse
+
+
+def flex_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block_mask: BlockMask,
+                          out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                          score: Optional[ScoreSpec] = None, mask: Optional[MaskSpec] = None,
+                          scale: Optional[float] = None):
+    """flex_attn_fwd that allocates nothing (C: flex_attn_fwd_noalloc).
+
+    ``out`` (and ``lse``, if wanted) are the caller's; the split-KV scratch is
+    the library's per-GPU array.  Calls that overlap in time on one GPU race.
+    Returns (out, lse)."""
+    lib = load_library()
+    score = score or ScoreSpec()
+    mask = mask or MaskSpec()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k and v must be 4-D (B, H, seq, D)")
+    B, Hq, L, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D or v.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPES:
+        raise ValueError("q, k, v must share a dtype, float32 or bfloat16")
+    _require_qkv(q, k, v)
+    dev = q.device
+    _require(out, "out", dev, dtype=q.dtype, shape=(B, Hq, L, D))
+    if lse is not None:
+        _require(lse, "lse", dev, dtype=torch.float32, shape=(B, Hq, L))
+    block_mask._validate(dev)
+    _require_mask_tensors(mask, dev, B)
+    st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    cs, cm, cbm = score.to_c(), mask.to_c(L, S), block_mask.to_c()
+    _check(lib.flex_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D,
+                                     st(q), st(k), st(v), ctypes.c_float(0.0 if scale is None else float(scale)),
+                                     ctypes.byref(cs), ctypes.byref(cm), ctypes.byref(cbm), out.data_ptr(),
+                                     None if lse is None else lse.data_ptr(),
+                                     ctypes.c_void_p(_stream_ptr(dev))))
     return out, lse
 
 

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdarg>
+#include <mutex>
 #include <string>
 
 #include "flexmi.h"
@@ -454,6 +455,72 @@ flex_status flex_attn_fwd_aux(const void* q, const void* k, const void* v, int32
     g_last_error.clear();
     return fwd_common(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, scale, score, mask, bm,
                       nullptr, out, lse, max_scores, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The forward without a caller workspace, for callers that cannot allocate.
+// The split-KV decode partials go to a file-scope device array instead; each
+// GPU holds its own copy, found once per device through hipGetSymbolAddress.
+// Nothing in it must start at zero: every decode workgroup writes all of its
+// rows' partials (zero-tile splits write an empty partial) before the combine
+// kernel, later on the same stream, reads them.
+namespace {
+
+constexpr size_t kScratchBytes = FLEX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch` (set up on the first call
+// per device, with that device current).
+flex_status scratch_for_device(int dev, void** ptr) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(FLEX_ERR_PARAM, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || p == nullptr)
+            return fail(FLEX_ERR_HIP, "scratch array of device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FLEX_OK;
+}
+
+}  // namespace
+
+flex_status flex_attn_fwd_noalloc(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                                  const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                                  const flex_score_params* score, const flex_mask_params* mask,
+                                  const flex_block_mask* bm, void* out, float* lse, void* stream) {
+    g_last_error.clear();
+    if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
+                                  bm, out, lse))
+        return s;
+    const size_t need = attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, (int)L, (int)S, D, bm->q_block, bm->kv_block,
+                                                 bm->num_kv_blocks, bm->B, bm->H);
+    if (need > kScratchBytes)
+        return fail(FLEX_ERR_WORKSPACE, "this call needs %zu bytes of scratch, above the %zu of the no-allocation entry",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        int dev = -1;
+        hipError_t e = stream ? hipStreamGetDevice(as_stream(stream), &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(FLEX_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+        if (flex_status st = scratch_for_device(dev, &ws)) return st;
+    }
+    return fwd_common(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, scale, score, mask, bm,
+                      nullptr, out, lse, nullptr, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 flex_status flex_attn_fwd_paged(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,

@@ -432,3 +432,28 @@ def test_binding_rejects_host_tensors_before_any_launch():
     bad = pbs.BlockMask(i32(1, 1, 2), i32(1, 1, 1, 1), i32(1, 1, 1), i32(1, 1, 1, 1), 64, 64, 64, 64)
     with pytest.raises(ValueError, match="shape|must be on"):
         bad._validate(torch.device("cpu"))
+
+
+def test_noalloc_entry_point_checks(lib):
+    """flex_attn_fwd_noalloc takes flex_attn_fwd's checks, and refuses before
+    any HIP call a call whose split-KV partials exceed its scratch array."""
+    lib.flex_attn_fwd_noalloc.restype = ctypes.c_int
+    a3 = lambda x: (ctypes.c_int64 * 3)(*x)
+
+    def call(f):
+        return lib.flex_attn_fwd_noalloc(f.q, f.k, f.v, f.dtype, f.B, f.Hq, f.Hkv, f.L, f.S, f.D, a3(f.qs), a3(f.ks),
+                                         a3(f.vs), ctypes.c_float(f.scale), ctypes.byref(f.score),
+                                         ctypes.byref(f.mask), ctypes.byref(f.bm), f.out, f.lse, None)
+    f = Fwd()
+    f.q = None
+    assert call(f) == NULL
+    f = Fwd(Hq=4, Hkv=1)
+    f.bm.num_kv_blocks = 3
+    assert call(f) == BLOCKMASK
+    # 1000 (batch, K/V head) units of 64 packed rows: one split each, 125*32*16 rows of
+    # (128 + 4) floats = 33.8 MB of partials, above the 32 MiB array
+    f = Fwd(B=125, Hq=32, Hkv=8, L=16, S=2048, D=128, qb=16)
+    need = lib.flex_attn_fwd_workspace_bytes(f.dtype, f.B, f.Hq, f.Hkv, f.L, f.S, f.D, ctypes.byref(f.bm))
+    assert need > 32 << 20
+    assert call(f) == WORKSPACE
+    assert "scratch" in pbs.flex_last_error()
