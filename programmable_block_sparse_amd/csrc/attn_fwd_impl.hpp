@@ -840,7 +840,8 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
                                                 const int* __restrict__ part_idx, int n_part,
                                                 const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                                 const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
-                                                f32x16_t (&o)[D / 32], RowState<false>& st, char* lds, int S, int b) {
+                                                f32x16_t (&o)[D / 32], RowState<false>& st, char* lds, int S, int b,
+                                                int rot = 0) {
     using G = Tiles<__bf16, D>;
     static_assert(STAGES >= 2, "at least double buffering");
     const int tid = threadIdx.x;
@@ -848,7 +849,15 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     const int sub_per_block = a.kv_block / kTileN;
     const bool with_doc = a.mask.uses_doc != 0;
 
+    // tiles are walked starting `rot` tiles into the range, wrapping around
+    // (any order gives the same result up to rounding)
+    const int n_range = tile_hi - tile_lo;
     auto tile_kv0 = [&](int t, bool& masked) -> int {
+        if (rot != 0) {
+            int u = t - tile_lo + rot;
+            if (u >= n_range) u -= n_range;
+            t = tile_lo + u;
+        }
         const int blk = sub_per_block == 1 ? t : t / sub_per_block;
         const int sub = t - blk * sub_per_block;
         int kb;
@@ -956,10 +965,10 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
                                             const int* __restrict__ full_idx, int tile_lo, int tile_hi,
                                             const TileConsts& tc, const LaneRow& row, bool wave_active, int kh,
                                             f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds, int S,
-                                            int b) {
+                                            int b, int rot = 0) {
     if constexpr (sizeof(T) == 2) {
         attend_rows_dma<D, SCORE, FIXED, KSPLIT, EXT, STAGES, PAGED>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
-                                                         tile_hi, tc, row, wave_active, kh, o, st, lds, S, b);
+                                                         tile_hi, tc, row, wave_active, kh, o, st, lds, S, b, rot);
     } else {
     using G = Tiles<T, D>;
     const LdsAddr<T, D> la{};
@@ -1093,10 +1102,6 @@ __device__ __forceinline__ int lane_doc(const MaskArgs& m, int q_pos) {
     return (q_pos >= 0 && q_pos < m.doc_len) ? __ldg(m.doc_id + q_pos) : -2;
 }
 
-// Waves per SIMD the prefill kernel is compiled for: four for bf16 key-split
-// workgroups at head dim 64 (the score pipeline is VALU-bound there, so more
-// waves hide MFMA and LDS latency behind each other's VALU work), otherwise
-// as many as the registers of the wider tiles allow.
 // Per-batch view of the call (paged / per-batch kernels only): the logical position of
 // query row 0 and the number of valid keys of batch b, when the mask carries
 // per-batch arrays (values clamped into range), and the K/V base of the head
@@ -1124,9 +1129,15 @@ __device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, i
     return reinterpret_cast<const T*>(base) + off;
 }
 
+// Waves per SIMD the prefill kernel is compiled for: four for bf16 key-split
+// workgroups at head dim 64 (the score pipeline is VALU-bound there, so more
+// waves hide MFMA and LDS latency behind each other's VALU work), otherwise
+// as many as the registers of the wider tiles allow.  The extended kernels
+// (mask programs, max_scores) of 128-row workgroups at head dim 64 need more
+// than the 168 registers of three waves and would spill, so they take two.
 template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
     static constexpr int value =
-        sizeof(T) == 2 ? (D == 64 ? ((KSPLIT && !EXT) ? 4 : 3) : 2) : (D == 64 ? 2 : 1);
+        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 3 : 4) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
 };
 
 
@@ -1335,9 +1346,14 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     RowState<false> st{kNegInf, 0.0f, 0.0f, kNegInf};
+    // each workgroup starts its key range at a different tile, so the
+    // workgroups streaming at the same pace do not read addresses a whole
+    // range apart at the same moment
+    const int n_rng = t_hi - t_lo;
+    const int rot = n_rng > 1 ? (int)(((uint32_t)blockIdx.x * 2654435761u >> 12) % (uint32_t)n_rng) : 0;
     attend_rows<T, D, SCORE, FIXED, true, EXT, DecodeShape<D>::kStages, PAGED>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
                                                                    n_part, a.full_idx + row_id * a.nKB, t_lo, t_hi,
-                                                                   tc, row, wave_active, kh, o, st, lds, bv.S, b);
+                                                                   tc, row, wave_active, kh, o, st, lds, bv.S, b, rot);
     merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
 
     const float l = wave_half_sum(st.l);
@@ -1466,14 +1482,16 @@ hipError_t dispatch_ext(const FwdArgs& a, hipStream_t stream) {
 }
 
 // Program masks and the max_scores output run in separately compiled
-// "extended" kernels, so the common kernels keep their register budget; paged
-// caches and per-batch offsets and lengths in a third set (extended kernels
-// that also remap tiles and read per-batch values).
+// "extended" kernels, so the common kernels keep their register budget.
+// Paged caches and per-batch offsets and lengths (tiles remapped through the
+// page table, per-batch values read per workgroup) have their own kernels,
+// lean or extended by the same rule.
 template <typename T, int D, bool DECODE>
 hipError_t dispatch(const FwdArgs& a, hipStream_t stream) {
+    const bool ext = a.mask.kind == MASK_PROGRAM || a.max_scores != nullptr;
     if (a.page_table != nullptr || a.mask.q_offsets != nullptr || a.mask.kv_lens != nullptr)
-        return dispatch_ext<T, D, DECODE, true, true>(a, stream);
-    if (a.mask.kind == MASK_PROGRAM || a.max_scores != nullptr) return dispatch_ext<T, D, DECODE, true, false>(a, stream);
+        return ext ? dispatch_ext<T, D, DECODE, true, true>(a, stream) : dispatch_ext<T, D, DECODE, false, true>(a, stream);
+    if (ext) return dispatch_ext<T, D, DECODE, true, false>(a, stream);
     return dispatch_ext<T, D, DECODE, false, false>(a, stream);
 }
 
