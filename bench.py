@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
+    p.add_argument("--quick", action="store_true",
+                   help="profiling runs: no time-based warm-up and one timing window of --steps calls per unit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")
     return p.parse_args()
@@ -230,7 +232,7 @@ def main():
     if not args.eager:
         runners = graph_runners(runners, dev, ([out, lse], step))
         mode = "hip_graph"
-    tm = time_units(runners, args, dev)
+    tm = time_units(runners, args, dev, **QUICK) if args.quick else time_units(runners, args, dev)
     ms_step, ms_fwd, ms_mask = tm["ms_per_step"], tm["fwd"]["median_ms"], tm["mask"]["median_ms"]
     print(f"bench: step {ms_step * 1e3:.1f} us ({args.steps} steps; windows median "
           f"{tm['step']['median_ms'] * 1e3:.1f} us), fwd {ms_fwd * 1e3:.1f} us "
@@ -344,6 +346,10 @@ def graph_runners(runners, dev, check):
     return graphs
 
 
+# --quick: for runs under a profiler, where every call is recorded
+QUICK = {"windows": 1, "min_calls": 1, "warm_ms": 0.0}
+
+
 def time_units(units, args, dev, windows=5, min_calls=50, warm_ms=100.0):
     """Time every unit on the stream its kernels run on (HIP events).
 
@@ -367,7 +373,7 @@ def time_units(units, args, dev, windows=5, min_calls=50, warm_ms=100.0):
         return start.elapsed_time(end)
 
     warm, warm_calls = 0.0, 0
-    while warm < warm_ms:
+    while warm_calls == 0 or warm < warm_ms:
         warm += window(units["step"], 20)
         warm_calls += 20
     ms_per_step = window(units["step"], args.steps) / args.steps
@@ -458,7 +464,7 @@ def main_bwd(args):
     if not args.eager:
         runners = graph_runners(runners, dev, ([out, lse, dq, dk, dv], step))
         mode = "hip_graph"
-    tm = time_units(runners, args, dev)
+    tm = time_units(runners, args, dev, **QUICK) if args.quick else time_units(runners, args, dev)
     ms_step, ms_bwd, ms_tr = tm["ms_per_step"], tm["bwd"]["median_ms"], tm["transpose"]["median_ms"]
     print(f"bench: step {ms_step * 1e3:.1f} us, bwd {ms_bwd * 1e3:.1f} us "
           f"[{tm['bwd']['min_ms'] * 1e3:.1f}, {tm['bwd']['max_ms'] * 1e3:.1f}], transpose {ms_tr * 1e3:.1f} us "
@@ -600,7 +606,8 @@ def cpu_baseline(args, w, inp, out, lse, flops):
         "cpu_blockmask_oracle_s": t_bm,
         "visible_element_flops": 4 * w.D * visible * w.B * w.Hq,
         "parity_on_bench_buffers": {"out_max_abs": err_o, "lse_max_abs": err_l, "neg_inf_pattern_equal": inf_ok,
-                                    "rows_checked": len(sample) * w.L, "slices": [list(p) for p in sample],
+                                    "rows_checked": len(sample) * w.L, "slices_checked": len(sample),
+                                    "last_slice": list(sample[-1]),
                                     "tolerance": {"out": tol_out, "lse": 1e-3}, "within_tolerance": within},
     }
 
