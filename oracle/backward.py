@@ -22,11 +22,17 @@ that definition, not anything printed on the pages:
 Under GQA the K/V gradients of a K/V head sum over its query heads.  Rows
 with no visible key have P = 0 and contribute nothing.  Nothing is blocked:
 each (batch, head) forms the full score matrix.
+
+As in the forward oracle, ``q_offset`` and the filled key length ``kv_len``
+(the blog's decode section: keys at or past a cache's valid length are not
+visible whatever the mask says) may be given per batch; a key that is not
+visible to any row gets zero dK and dV.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .attention import _at
 from .mods import ScoreMod, MaskMod, SOFTCAP, SOFTCAP_ALIBI
 
 
@@ -39,10 +45,12 @@ def score_derivative(score: ScoreMod, s):
     return np.ones_like(s)
 
 
-def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset: int, pairs=None,
-                       row_chunk: int = 0):
+def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: MaskMod, q_offset, pairs=None,
+                       row_chunk: int = 0, kv_len=None):
     """(dq, dk, dv) in float64 for (B, Hq, L, D) queries and (B, Hkv, S, D) keys/values.
 
+    ``q_offset``: logical position of query row 0, an int or one per batch.
+    ``kv_len``: None (all S keys), or the valid key count, an int or one per batch.
     ``pairs``: optional list of (batch, query head) to include; the gradients
     then hold only those heads' terms (the others stay zero).  Default: all.
     ``row_chunk``: process that many query rows at a time (0: all); rows are
@@ -58,7 +66,6 @@ def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: Ma
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    q_pos = (np.arange(L, dtype=np.int64) + int(q_offset))[:, None]
     kv = np.arange(S, dtype=np.int64)[None, :]
     if pairs is None:
         pairs = [(b, h) for b in range(B) for h in range(Hq)]
@@ -66,11 +73,15 @@ def attention_backward(q, k, v, dout, *, scale: float, score: ScoreMod, mask: Ma
     for b, h in pairs:
         hk = h // group
         K, V = k[b, hk], v[b, hk]
+        q_pos = (np.arange(L, dtype=np.int64) + int(_at(q_offset, b)))[:, None]
+        kl = _at(kv_len, b)
         for r0 in range(0, L, step):
             rows = slice(r0, min(L, r0 + step))
             qp = q_pos[rows]
             s = (q[b, h, rows] @ K.T) * float(scale)
             vis = mask(b, h, qp, kv)
+            if kl is not None:
+                vis = vis & (kv < int(kl))
             z = np.where(vis, score(s, b, h, qp, kv, Hq), -np.inf)
             live = vis.any(axis=1)
             P = np.zeros_like(z)

@@ -72,6 +72,38 @@ def test_gradients_match_finite_differences(name, score, mask, q_offset):
         assert np.allclose(g, fd, rtol=1e-6, atol=1e-7), (name, np.abs(g - fd).max())
 
 
+def test_per_batch_offsets_and_lengths_match_finite_differences():
+    # per-batch query offsets and filled lengths (decode section of the blog),
+    # through the forward oracle's own per-batch handling
+    B, Hq, Hkv, L, S, D = 2, 2, 1, 4, 7, 4
+    q, k, v, do = _inputs(17, B, Hq, Hkv, L, S, D, qscale=1.2)
+    q_offsets, kv_lens = [2, -1], [5, 7]
+    score, mask = ScoreMod("softcap", cap=2.5), MaskMod("causal")
+    dq, dk, dv = attention_backward(q, k, v, do, scale=0.9, score=score, mask=mask, q_offset=q_offsets,
+                                    kv_len=kv_lens)
+
+    def f():
+        out, _ = attention(q, k, v, scale=0.9, score=score, mask=mask, q_offset=q_offsets, kv_len=kv_lens)
+        return float((out * do).sum())
+
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = _fd_grad(x, f)
+        assert np.allclose(g, fd, rtol=1e-6, atol=1e-7), np.abs(g - fd).max()
+    # keys past a batch's filled length get nothing
+    assert np.all(dk[0, :, 5:] == 0) and np.all(dv[0, :, 5:] == 0)
+
+
+def test_filled_length_equals_truncated_cache():
+    # kv_len = n is the same problem as a cache holding only the first n keys
+    q, k, v, do = _inputs(19, 1, 4, 2, 6, 10, 8)
+    kw = dict(scale=0.6, score=ScoreMod("alibi", alibi_m=4.0), mask=MaskMod("causal"), q_offset=3)
+    dq, dk, dv = attention_backward(q, k, v, do, kv_len=7, **kw)
+    dq2, dk2, dv2 = attention_backward(q, k[:, :, :7], v[:, :, :7], do, **kw)
+    assert np.allclose(dq, dq2, rtol=0, atol=1e-13)
+    assert np.allclose(dk[:, :, :7], dk2, rtol=0, atol=1e-13) and np.all(dk[:, :, 7:] == 0)
+    assert np.allclose(dv[:, :, :7], dv2, rtol=0, atol=1e-13) and np.all(dv[:, :, 7:] == 0)
+
+
 def test_empty_rows_have_zero_query_gradient():
     # q_offset -2 under causal: rows 0 and 1 see no key
     q, k, v, do = _inputs(3, 1, 2, 2, 4, 6, 8)
