@@ -55,20 +55,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
-// Soft-cap polynomials (iteratively reweighted least-squares fits of odd
-// polynomials, max abs error over the range evaluated in fp32):
-//   tanh(y) ~= y * (kTanh0 + kTanh1*y^2 + kTanh2*y^4) for |y| <= kTanhRange, 1.3e-6
-//   tanh(y) ~= y * (kLin0 + kLin1*y^2)                 for |y| <= kLinRange,  7.9e-6
-// The cubic is used only when cap * 7.9e-6 stays below kPolyScoreErr, a quarter
-// of the 1e-3 lse tolerance, i.e. for caps up to about 31.
+// Soft-cap polynomials: odd cubic and quintic approximations of tanh(y) on
+// [0, Y], minimax in absolute error, fitted on the host for each cap with the
+// largest range Y <= kTanhRange whose error times the cap stays below
+// kPolyScoreErr, a quarter of the 1e-3 lse tolerance (score_consts).
 constexpr double kTanhRange = 0.4;
-constexpr double kTanh0 = 0.9999788560769031;
-constexpr double kTanh1 = -0.3322550629897203;
-constexpr double kTanh2 = 0.11942884091924301;
-constexpr double kLinRange = 0.25;
-constexpr double kLin0 = 0.9998436637524046;
-constexpr double kLin1 = -0.32320621727400445;
-constexpr double kLinErr = 7.9e-6;
 constexpr double kPolyScoreErr = 2.5e-4;
 
 
@@ -136,7 +127,7 @@ struct TileConsts {
     float k0, k1, k2; // quintic path: g2 = acc*(k0 + k1*w + k2*w^2), w = acc^2
     float amax;       // quintic valid while |acc| <= amax
     float j0, j1;     // cubic path: g2 = acc*(j0 + j1*w)
-    float amax1;      // cubic valid while |acc| <= amax1 (0 when the cap is too large)
+    float amax1;      // cubic valid while |acc| <= amax1 (amax1 <= amax)
     float alpha2;     // distance-bias slope * log2e of this lane's query head
     float ref_fixed;  // fixed base-2 reference
     double scale_d, cap_d, alpha_d;
@@ -440,18 +431,19 @@ __device__ __forceinline__ void pack_p(bf16x8_t (&pb)[2], const float (&p)[16]) 
         for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)p[8 * t + e];
 }
 
-// Sum of the rounded probabilities (two per v_dot2 against a pair of ones).
-__device__ __forceinline__ float sum_packed(const bf16x8_t (&pb)[2]) {
+// acc plus the sum of the rounded probabilities (two per v_dot2 against a
+// pair of ones, in two independent chains).
+__device__ __forceinline__ float sum_packed(const bf16x8_t (&pb)[2], float acc) {
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float acc = 0.0f;
+    float part[2] = {acc, 0.0f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bf16x2_t pair = {pb[t][2 * e], pb[t][2 * e + 1]};
-            acc = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, acc, false);
+            part[t] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[t], false);
         }
-    return acc;
+    return part[0] + part[1];
 }
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -641,7 +633,7 @@ __device__ __forceinline__ void apply_mask(float (&z)[16], const MaskArgs& m, in
 // exponentials, so that work placed there (QK^T of the tile's other key half)
 // shares a basic block with the exponentials and PV and its MFMAs overlap
 // their VALU work.
-template <typename T, int D, int SCORE, bool FIXED, bool EXT, typename Mid>
+template <typename T, int D, int SCORE, bool FIXED, bool EXT, bool CUBIC_FIRST, typename Mid>
 __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __restrict__ buf,
                                             const LdsAddr<T, D>& la, f32x16_t (&o)[D / 32],
                                             RowState<Precise<T>::value>& st, const TileConsts& tc,
@@ -685,8 +677,13 @@ __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __res
             for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(s[r]));
             // polynomial tanh (cubic or quintic), or the exact form
             // cap - 2*cap / (1 + e^{2y}) when a score of the half is out of the
-            // polynomials' range (wave-uniform choice)
-            if (!__any(amax > tc.amax1)) {
+            // polynomials' range (wave-uniform choice).  With CUBIC_FIRST the
+            // cubic, the common case, is evaluated first in place and the other
+            // forms overwrite it: the compiler then does not give the cubic a
+            // branch of its own, whose results it copies (eight v_mov_b64 per
+            // half); the empty asm keeps it from sinking the cubic back into one.
+            // Kernels with less register room keep the plain three-way branch.
+            if constexpr (CUBIC_FIRST) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float x = base;
@@ -694,6 +691,20 @@ __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __res
                     const float acc = s[r];
                     const float poly = __builtin_fmaf(acc * acc, tc.j1, tc.j0);
                     z[r] = __builtin_fmaf(acc, poly, x);
+                    asm volatile("" : "+v"(z[r]));
+                }
+            }
+            if (!__any(amax > tc.amax1)) {
+                if constexpr (!CUBIC_FIRST) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float x = base;
+                        if constexpr (SCORE == SCORE_SOFTCAP_ALIBI)
+                            x = __builtin_fmaf(tc.alpha2, (float)acc_row(r, 0), base);
+                        const float acc = s[r];
+                        const float poly = __builtin_fmaf(acc * acc, tc.j1, tc.j0);
+                        z[r] = __builtin_fmaf(acc, poly, x);
+                    }
                 }
             } else if (!__any(amax > tc.amax)) {
 #pragma unroll
@@ -755,7 +766,18 @@ __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __res
         for (int r = 0; r < 16; ++r) {
             if constexpr (P) z[r] = expf(z[r]);
             else z[r] = __builtin_amdgcn_exp2f(z[r]);
-            lsum += z[r];
+            if constexpr (!CUBIC_FIRST) lsum += z[r];
+        }
+        if constexpr (CUBIC_FIRST) {
+            // pairwise sum: fifteen adds in four dependent steps
+            float t[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) t[r] = z[2 * r] + z[2 * r + 1];
+#pragma unroll
+            for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+                for (int r = 0; r < w; ++r) t[r] += t[r + w];
+            lsum = t[0];
         }
         st.l += lsum;
         if constexpr (P) {
@@ -764,7 +786,7 @@ __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __res
         } else {
             bf16x8_t pb[2];
             pack_p(pb, z);
-            st.lr += sum_packed(pb);
+            st.lr = sum_packed(pb, st.lr);
             pv_bf16<D>(o, pb, reinterpret_cast<const char*>(Vs), la, kb2_lds);
         }
     }
@@ -781,8 +803,8 @@ __device__ __forceinline__ void process_tile(const QRegs<T, D>& qr, const char* 
                                              const MaskArgs& mask, bool masked, int kv0, int S, const LaneRow& row,
                                              int kb2, int kb2_lds, int lane) {
     const f32x16_t s = qk_block<T, D>(qr, buf, la, sizeof(T) == 2 ? kb2_lds : kb2, lane);
-    tile_update<T, D, SCORE, FIXED, EXT>(s, buf, la, o, st, tc, mask, masked, kv0, S, row, kb2, kb2_lds, lane,
-                                         [] {});
+    tile_update<T, D, SCORE, FIXED, EXT, false>(s, buf, la, o, st, tc, mask, masked, kv0, S, row, kb2, kb2_lds, lane,
+                                                [] {});
 }
 
 // Both 32-key halves of a 64-key tile in one wave: QK^T of the second half is
@@ -793,11 +815,13 @@ __device__ __forceinline__ void process_tile_pair(const QRegs<T, D>& qr, const c
                                                   RowState<Precise<T>::value>& st, const TileConsts& tc,
                                                   const MaskArgs& mask, bool masked, int kv0, int S,
                                                   const LaneRow& row, int lane) {
+    constexpr bool kCubicFirst = D == 64 && FIXED && !EXT;
     const f32x16_t s0 = qk_block<T, D>(qr, buf, la, 0, lane);
     f32x16_t s1;
-    tile_update<T, D, SCORE, FIXED, EXT>(s0, buf, la, o, st, tc, mask, masked, kv0, S, row, 0, 0, lane,
-                                         [&] { s1 = qk_block<T, D>(qr, buf, la, 1, lane); });
-    tile_update<T, D, SCORE, FIXED, EXT>(s1, buf, la, o, st, tc, mask, masked, kv0, S, row, 1, 1, lane, [] {});
+    tile_update<T, D, SCORE, FIXED, EXT, kCubicFirst>(s0, buf, la, o, st, tc, mask, masked, kv0, S, row, 0, 0, lane,
+                                                      [&] { s1 = qk_block<T, D>(qr, buf, la, 1, lane); });
+    tile_update<T, D, SCORE, FIXED, EXT, kCubicFirst>(s1, buf, la, o, st, tc, mask, masked, kv0, S, row, 1, 1, lane,
+                                                      [] {});
 }
 
 // True when a wave whose 32 rows start at query position q_lo sees no key of
@@ -1133,11 +1157,11 @@ __device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, i
 // workgroups at head dim 64 (the score pipeline is VALU-bound there, so more
 // waves hide MFMA and LDS latency behind each other's VALU work), otherwise
 // as many as the registers of the wider tiles allow.  The extended kernels
-// (mask programs, max_scores) of 128-row workgroups at head dim 64 need more
-// than the 168 registers of three waves and would spill, so they take two.
+// (mask programs, max_scores) at head dim 64 need more than the 168 registers
+// of three waves and would spill, so they take two.
 template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
     static constexpr int value =
-        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 3 : 4) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
+        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 2 : 4) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
 };
 
 

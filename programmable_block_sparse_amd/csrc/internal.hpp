@@ -73,7 +73,7 @@ struct ScoreConsts {
     float k0, k1, k2; // quintic path: g2 = acc*(k0 + k1*w + k2*w^2), w = acc^2
     float amax;       // quintic valid while |acc| <= amax
     float j0, j1;     // cubic path: g2 = acc*(j0 + j1*w)
-    float amax1;      // cubic valid while |acc| <= amax1 (0 when the cap is too large)
+    float amax1;      // cubic valid while |acc| <= amax1 (amax1 <= amax)
 };
 
 // Forward pass arguments (element strides; last dim contiguous).
