@@ -376,8 +376,10 @@ size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32
  *                (-inf rows, which saw no key, receive zero gradients)
  *   bm, bmq      the BlockMask of that call and its Q-side lists
  *                (flex_blockmask_transpose); q_block 64 or 128, kv_block a
- *                multiple of 64; contiguous caches only, and no per-batch
- *                q_offsets / kv_lens (UNSUPPORTED)
+ *                multiple of 64 (UNSUPPORTED otherwise); contiguous K/V
+ *   mask         may carry per-batch q_offsets / kv_lens as in the forward
+ *                (the BlockMask then has B rows); keys at or past a batch's
+ *                kv_lens are visible to no row and get zero dk, dv
  *   dq           device (B,Hq,L,D) contiguous, dtype `dtype`
  *   dk, dv       device (B,Hkv,S,D) contiguous, dtype `dtype`
  *   workspace    device scratch of at least flex_attn_bwd_workspace_bytes(),

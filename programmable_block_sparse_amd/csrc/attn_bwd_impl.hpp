@@ -188,13 +188,14 @@ __device__ __forceinline__ void qk2_block(const QRegs<T, D>& ra, const QRegs<T, 
 // Visibility in the key-major orientation: bit o of the result says whether
 // this lane's key `key` is visible from query row qr0 + o (qr0 includes the
 // lane half's row offset; the rows used are o = acc_row(r, 0)).  Rows past L
-// and keys past S are hidden.  doc_rows holds the document ids of rows
-// qr0 + 0..27 (LDS).
+// and keys past S (the batch's filled length) are hidden.  q_off is the
+// batch's position of query row 0.  doc_rows holds the document ids of rows
+// qr0 + 0..27 (LDS); a row whose position lies outside doc_id has no document.
 template <bool EXT>
-__device__ __forceinline__ uint32_t mask_bits_keys(const MaskArgs& m, int key, int S, int L, int qr0, int hq,
-                                                   int doc_k, const int* __restrict__ doc_rows) {
-    const int p0i = qr0 + m.q_offset;                        // position of row offset 0 (|p0| < 2^30)
-    const int64_t p0 = p0i;
+__device__ __forceinline__ uint32_t mask_bits_keys(const MaskArgs& m, int key, int S, int L, int qr0, int q_off,
+                                                   int hq, int doc_k, const int* __restrict__ doc_rows) {
+    const int p0i = qr0 + q_off;                             // position of row offset 0, in [-2^30, 2^31)
+    const int64_t p0 = (int64_t)qr0 + q_off;
     uint32_t keep = key < S ? range_bits(0, (int64_t)L - qr0) : 0u;
     const uint32_t causal = range_bits((int64_t)key - p0, 32);  // key <= p0 + o
     auto doc_bits = [&]() __attribute__((always_inline)) -> uint32_t {
@@ -206,7 +207,7 @@ __device__ __forceinline__ uint32_t mask_bits_keys(const MaskArgs& m, int key, i
 #pragma unroll
             for (int e = 0; e < 4; ++e) bits |= (dv[e] == doc_k) ? (1u << (8 * g + e)) : 0u;
         }
-        return bits;
+        return bits & range_bits(-p0, (int64_t)m.doc_len - p0);
     };
     switch (m.kind) {
     case MASK_NOOP: break;
@@ -238,8 +239,8 @@ __device__ __forceinline__ uint32_t mask_bits_keys(const MaskArgs& m, int key, i
                     break;
                 }
                 case PRED_STRIDE: {                                     // o = key - p0 (mod arg)
-                    // 32-bit residues (key >= 0, |p0| < 2^30): key - p0 itself
-                    // may not fit in 32 bits
+                    // 32-bit residues (key >= 0, -2^30 <= p0 < 2^31): key - p0
+                    // itself may not fit in 32 bits
                     int p0m = p0i % arg;
                     if (p0m < 0) p0m += arg;
                     int rm = key % arg - p0m;
@@ -399,6 +400,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_rows(BwdArgs a) {
     }
 }
 
+// Position of query row 0 and the filled key length of batch b: the mask's
+// per-batch arrays when it carries them (values clamped as in the forward),
+// else its scalar offset and the capacity S.
+__device__ __forceinline__ int batch_q_offset(const MaskArgs& m, int b) {
+    return m.q_offsets != nullptr ? min(max(scalar_load(m.q_offsets + b), -(1 << 30)), 1 << 30) : m.q_offset;
+}
+__device__ __forceinline__ int batch_kv_len(const MaskArgs& m, int b, int S) {
+    return m.kv_lens != nullptr ? min(max(scalar_load(m.kv_lens + b), 0), S) : S;
+}
+
 // --------------------------------------------------------- key-major pass
 // Tiles of query head hq's Q-side list for KV block kvb (64-row tiles).
 __device__ __forceinline__ int bwd_head_tiles(const BwdArgs& a, int b, int hq, int kvb) {
@@ -458,6 +469,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
         bh = n % BH;
     }
     const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+    const int q_off = batch_q_offset(a.mask, b), S_b = batch_kv_len(a.mask, b, a.S);
     const int kvb = kt / subs;
     const int kv0 = kt * kTileN;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), hf = lane >> 5;
@@ -539,11 +551,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
             f32x16_t s, dp;
             qk2_block<T, D>(kr, vr, cur, cur + G::kTileBytes, la, kb2, lane, s, dp);
             float z[16], pg[16];
-            scores2<SCORE, Precise<T>::value>(s, bc.alpha2 * (float)(key - (qr0 + a.mask.q_offset)), -bc.alpha2, bc,
-                                              z, pg);
+            scores2<SCORE, Precise<T>::value>(s, bc.alpha2 * (float)(key - (qr0 + q_off)), -bc.alpha2, bc, z, pg);
             if (masked) {
                 const uint32_t keep =
-                    mask_bits_keys<EXT>(a.mask, key, a.S, a.L, qr0, hq, doc_k,
+                    mask_bits_keys<EXT>(a.mask, key, S_b, a.L, qr0, q_off, hq, doc_k,
                                         reinterpret_cast<const int*>(cur + G::kDocOffset) + 32 * qh + 4 * hf);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) z[r] = (keep >> acc_row(r, 0)) & 1u ? z[r] : kNegInf;
@@ -594,9 +605,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
                 else if (wave == 1)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + G::kStatsOffset + 256), 4, l4,
                                                              q0 * 4, 0, 0);
-                else if (wave == 2 && with_doc)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, l4,
-                                                             (q0 + a.mask.q_offset) * 4, 0, 0);
+                else if (wave == 2 && with_doc) {
+                    // rows whose position is outside doc_id read 0 (out of
+                    // range); mask_bits_keys hides them
+                    const int pos = q0 + q_off + l4 / 4;
+                    const int voff = (pos >= 0 && pos < a.mask.doc_len) ? pos * 4 : 0x7ffffff0;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, voff, 0, 0,
+                                                             0);
+                }
             };
             walk_ring<true>(n_tiles, desc, issue, compute, lds, G::kBufBytes);
         } else {
@@ -611,7 +627,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
                 } else if (tid < 128) {
                     reinterpret_cast<float*>(buf + G::kStatsOffset)[tid] = sslice[q0 + tid - 64];
                 } else if (tid < 192) {
-                    const int pos = q0 + (tid - 128) + a.mask.q_offset;
+                    const int pos = q0 + (tid - 128) + q_off;
                     int d = -1;
                     if (with_doc && pos >= 0 && pos < a.mask.doc_len) d = a.mask.doc_id[pos];
                     reinterpret_cast<int*>(buf + G::kDocOffset)[tid - 128] = d;
@@ -734,6 +750,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
         bh = (xcd + 8 * (k / a.group)) * a.group + k % a.group;
     }
     const int b = bh / a.Hq, hq = bh % a.Hq, hkv = hq / a.group;
+    const int S_b = batch_kv_len(a.mask, b, a.S);
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), hf = lane >> 5;
     const int rg = wave & 1, kh = wave >> 1;
     const bool with_doc = a.mask.uses_doc != 0;
@@ -741,7 +758,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     LaneRow row;
     row.q_row = qb * a.q_block + part * 64 + rg * 32 + (lane & 31);
     row.ok = row.q_row < a.L;
-    row.q_pos = row.q_row + a.mask.q_offset;
+    row.q_pos = row.q_row + batch_q_offset(a.mask, b);
     row.hq = hq;
     row.doc_q = lane_doc(a.mask, row.q_pos);
 
@@ -797,7 +814,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
         const int key_base = kv0 + 32 * kh + 4 * hf;
         float z[16], ds[16];
         scores2<SCORE, Precise<T>::value>(s, bc.alpha2 * (float)(key_base - row.q_pos), bc.alpha2, bc, z, ds);
-        if (masked) apply_mask<EXT>(z, a.mask, kv0, a.S, row, reinterpret_cast<const int*>(cur + G::kDocOffset), kh, hf);
+        if (masked) apply_mask<EXT>(z, a.mask, kv0, S_b, row, reinterpret_cast<const int*>(cur + G::kDocOffset), kh, hf);
 #pragma unroll
         for (int r = 0; r < 16; ++r) ds[r] *= __builtin_amdgcn_exp2f(z[r] - lse2) * (dp[r] - dsum);
         xtp<T, D>(dq, ds, cur, la, kb2, lane);   // dq^T += K^T dS^T

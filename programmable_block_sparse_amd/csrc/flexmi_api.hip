@@ -596,8 +596,6 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
         return fail(FLEX_ERR_BLOCKMASK, "Q-side block mask dims differ from the block mask's");
     if (bm->q_block != 64 && bm->q_block != 128)
         return fail(FLEX_ERR_UNSUPPORTED, "the backward pass needs q_block 64 or 128 (got %d)", bm->q_block);
-    if (per_batch(mask))
-        return fail(FLEX_ERR_UNSUPPORTED, "the backward pass takes no per-batch q_offsets / kv_lens");
     if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return fail(FLEX_ERR_LAYOUT, "dout, dq, dk and dv must be 16-byte aligned");

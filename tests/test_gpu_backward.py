@@ -27,8 +27,8 @@ import pytest
 import torch
 
 import programmable_block_sparse_amd as pbs
-from gpu_common import require_gpu
-from oracle import MaskMod, ScoreMod, attention_backward, build_block_mask, transpose_block_mask
+from gpu_common import assert_attention_close, assert_block_mask_equal, require_gpu
+from oracle import MaskMod, ScoreMod, attention, attention_backward, build_block_mask, transpose_block_mask
 from oracle import default_scale as oracle_default_scale
 from workloads import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, make_upstream
 from workloads.torch_io import specs, to_device
@@ -210,6 +210,89 @@ def test_bwd_programs(dev, pi):
         run_bwd_case(dev, seed=90 + pi, dtype=dtype, B=1, Hq=4, Hkv=2, L=230, S=230, D=D, qb=64, kb=64,
                      score=dict(kind="softcap_alibi", cap=20.0), mask_kind="program", clauses=clauses,
                      bm_heads=heads, what=f"program {pi} {dtype}")
+
+
+def _i32(x, dev):
+    return torch.tensor(np.asarray(x, dtype=np.int32), device=dev)
+
+
+def run_bwd_per_batch(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, mask_kind, offs, lens, window=0,
+                      sinks=0, clauses=(), doc_max=0, split_cols=False, what=""):
+    """Backward with per-batch query offsets and filled key lengths (the
+    blog's decode section: a cache's capacity S is not its filled length).
+    The GPU BlockMask and forward are checked against the oracle first, so a
+    failure names the stage; then the gradients, including zero dk, dv rows
+    for keys at or past each batch's length."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    do = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    clauses = tuple(tuple(c) for c in clauses)
+    doc_np = doc_t = None
+    if mask_kind == "doc_causal" or any(n == "doc" for c in clauses for n, _ in c):
+        # ids for positions [0, max(S, L)); query positions outside have no document
+        doc_np = _many_docs(rng, max(S, L), doc_max)
+        doc_t = torch.from_numpy(doc_np).to(dev)
+    spec = pbs.MaskSpec(kind=mask_kind, window=window, sinks=sinks, q_offset=0, doc_id=doc_t, clauses=clauses,
+                        q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev))
+    mod = MaskMod(mask_kind, window=window, sinks=sinks, doc_id=doc_np, clauses=clauses)
+    heads = Hq if any(n == "head_lt" for c in clauses for n, _ in c) else 1
+    bm = pbs.flex_blockmask_build(spec, L, S, qb, kb, B=B, H=heads, device=dev)
+    assert_block_mask_equal(bm, build_block_mask(mod, L, S, qb, kb, B=B, H=heads, q_offset=offs, kv_len=lens))
+    bmq = pbs.flex_blockmask_transpose(bm)
+    sspec, smod = pbs.ScoreSpec(**score), ScoreMod(**score)
+    qt, kt, vt, dot = (_tensor(x, dtype, dev) for x in (q, k, v, do))
+    out, lse = pbs.flex_attn_fwd(qt, kt, vt, block_mask=bm, score=sspec, mask=spec)
+    grads = pbs.flex_attn_bwd(qt, kt, vt, out, dot, lse, block_mask=bm, block_mask_q=bmq, score=sspec, mask=spec)
+    if split_cols:
+        ws = pbs.flex_attn_bwd_workspace_bytes(qt.dtype, B, Hq, Hkv, L, S, D, bm)
+        assert ws > 2 * B * Hq * ((L + 127) // 128 * 128) * 4, "case does not split long columns"
+    torch.cuda.synchronize()
+    sc = oracle_default_scale(D)
+    qw, kw, vw, dw = (_widen(x, dtype) for x in (q, k, v, do))
+    out_ref, lse_ref = attention(qw, kw, vw, scale=sc, score=smod, mask=mod, q_offset=offs, kv_len=lens)
+    assert_attention_close(out, lse, out_ref, lse_ref, dtype, f"{what} forward")
+    ref = attention_backward(qw, kw, vw, dw, scale=sc, score=smod, mask=mod, q_offset=offs, kv_len=lens)
+    assert_grads_close(grads, ref, dtype, what)
+    for b, n in enumerate(lens):
+        if n < S:
+            assert grads[1][b, :, n:].float().abs().max().item() == 0, f"{what}: dk of batch {b} past its length"
+            assert grads[2][b, :, n:].float().abs().max().item() == 0, f"{what}: dv of batch {b} past its length"
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_bwd_per_batch_offsets_and_lengths(dev, dtype, D):
+    run_bwd_per_batch(dev, seed=400 + D, dtype=dtype, B=3, Hq=4, Hkv=2, L=150, S=400, D=D, qb=64, kb=64,
+                      score=dict(kind="softcap_alibi", cap=20.0, alibi_m=8.0), mask_kind="causal",
+                      offs=[250, 0, 40], lens=[400, 130, 230], what=f"per-batch causal {dtype} D={D}")
+    run_bwd_per_batch(dev, seed=410 + D, dtype=dtype, B=2, Hq=2, Hkv=1, L=130, S=300, D=D, qb=128, kb=64,
+                      score=dict(kind="softcap", cap=5.0), mask_kind="causal_window_sinks", window=60, sinks=3,
+                      offs=[170, -20], lens=[300, 77], what=f"per-batch window {dtype} D={D}")
+    run_bwd_per_batch(dev, seed=420 + D, dtype=dtype, B=2, Hq=4, Hkv=4, L=100, S=260, D=D, qb=64, kb=128,
+                      score=dict(kind="alibi", alibi_m=4.0), mask_kind="noop", offs=[0, 0], lens=[260, 1],
+                      what=f"per-batch lengths noop {dtype} D={D}")
+
+
+def test_bwd_per_batch_documents_and_programs(dev):
+    # query positions before 0 or past the id array have no document
+    run_bwd_per_batch(dev, seed=430, dtype="bf16", B=3, Hq=2, Hkv=1, L=200, S=500, D=64, qb=64, kb=64,
+                      score=dict(kind="none"), mask_kind="doc_causal", offs=[-30, 120, 400], lens=[500, 330, 500],
+                      doc_max=90, what="per-batch documents")
+    run_bwd_per_batch(dev, seed=431, dtype="f32", B=2, Hq=2, Hkv=2, L=120, S=300, D=64, qb=64, kb=64,
+                      score=dict(kind="softcap", cap=10.0), mask_kind="doc_causal", offs=[250, -60], lens=[300, 200],
+                      doc_max=70, what="per-batch documents f32")
+    for pi, clauses in enumerate(PROGRAMS):
+        run_bwd_per_batch(dev, seed=440 + pi, dtype="bf16", B=2, Hq=4, Hkv=2, L=160, S=330, D=64, qb=64, kb=64,
+                          score=dict(kind="softcap_alibi", cap=20.0), mask_kind="program", clauses=clauses,
+                          offs=[170, -7], lens=[330, 150], doc_max=80, what=f"per-batch program {pi}")
+
+
+def test_bwd_per_batch_long_columns(dev):
+    # columns long enough to be split across workgroups, with lengths
+    run_bwd_per_batch(dev, seed=450, dtype="bf16", B=2, Hq=8, Hkv=1, L=1100, S=1100, D=64, qb=128, kb=64,
+                      score=dict(kind="softcap", cap=20.0), mask_kind="noop", offs=[0, 0], lens=[1100, 700],
+                      split_cols=True, what="per-batch split columns")
 
 
 @pytest.mark.parametrize("D,L,sinks", [(64, 300, 0), (128, 300, 0), (128, 1100, 4)])
