@@ -377,6 +377,7 @@ size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32
  *   bm, bmq      the BlockMask of that call and its Q-side lists
  *                (flex_blockmask_transpose); q_block 64 or 128, kv_block a
  *                multiple of 64 (UNSUPPORTED otherwise); contiguous K/V
+ *                (paged pools: flex_attn_bwd_paged)
  *   mask         may carry per-batch q_offsets / kv_lens as in the forward
  *                (the BlockMask then has B rows); keys at or past a batch's
  *                kv_lens are visible to no row and get zero dk, dv
@@ -431,6 +432,26 @@ flex_status flex_attn_fwd_paged(const void* q, const void* k, const void* v, int
                                 const flex_score_params* score, const flex_mask_params* mask,
                                 const flex_block_mask* bm, const flex_kv_pages* pages, void* out, float* lse,
                                 float* max_scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* flex_attn_bwd over a paged K/V cache: the gradients for a forward run by
+ * flex_attn_fwd_paged (same pools, pages, strides, S and mask).  The
+ * key-major pass reads each 64-key tile's K and V rows from the page holding
+ * them, the query-major pass stages its tiles from there, as the forward does.
+ * dk and dv are the gradients of the LOGICAL keys and values: device
+ * (B, Hkv, S, D) contiguous, row j of batch b for logical key j (a caller
+ * that trains through a pool scatters them back through its page table, where
+ * pages shared between batches add up).  Every other argument is as for
+ * flex_attn_bwd.
+ * Errors: as flex_attn_bwd, plus NULL (pages, page_table), PARAM (page
+ * geometry). */
+flex_status flex_attn_bwd_paged(const void* q, const void* k, const void* v, const flex_kv_pages* pages,
+                                const void* out, const void* dout, const float* lse, int32_t dtype, int32_t B,
+                                int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D,
+                                const int64_t q_strides[3], const int64_t k_strides[3],
+                                const int64_t v_strides[3], float scale, const flex_score_params* score,
+                                const flex_mask_params* mask, const flex_block_mask* bm,
+                                const flex_block_mask_q* bmq, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Size of the device scratch array behind flex_attn_fwd_noalloc (per GPU). */
 #define FLEX_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)

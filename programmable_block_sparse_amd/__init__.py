@@ -11,7 +11,9 @@ the same names:
   flex_attn_fwd_paged(q, k_pool, v_pool, page_table, S=..., ...) -> (out, lse, max_scores)
   flex_attn_fwd_workspace_bytes(...)
   flex_blockmask_transpose(block_mask) -> BlockMaskQ
+  flex_attn_fwd_noalloc(q, k, v, ...) -> (out, lse)
   flex_attn_bwd(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
+  flex_attn_bwd_paged(q, k_pool, v_pool, page_table, out, dout, lse, S=..., ...) -> (dq, dk, dv)
   flex_attn_bwd_workspace_bytes(...)
   BlockMask.to_dense / grid / to_string / sparsity / [b, h, rows] / adjust
       (flex_blockmask_to_dense, _grid, _sparsity, _slice, _adjust)
@@ -34,7 +36,7 @@ __all__ = [
     "MaskSpec", "ScoreSpec", "BlockMask", "FlexError", "load_library", "library_path",
     "flex_blockmask_build", "flex_attn_fwd", "flex_attn_fwd_aux", "flex_attn_fwd_workspace_bytes",
     "BlockMaskQ", "flex_blockmask_transpose", "flex_attn_bwd", "flex_attn_bwd_workspace_bytes",
-    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc",
+    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc", "flex_attn_bwd_paged",
     "flex_status_string", "flex_last_error", "MASK_KINDS", "SCORE_KINDS", "PREDICATES", "EXPORTED_SYMBOLS",
 ]
 
@@ -46,7 +48,7 @@ MAX_CLAUSES, MAX_LITERALS = 4, 2
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED_SYMBOLS = ("flex_blockmask_build", "flex_attn_fwd_workspace_bytes", "flex_attn_fwd", "flex_attn_fwd_aux",
                     "flex_blockmask_transpose", "flex_attn_bwd_workspace_bytes", "flex_attn_bwd",
-                    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc",
+                    "flex_attn_fwd_paged", "flex_attn_fwd_noalloc", "flex_attn_bwd_paged",
                     "flex_blockmask_to_dense", "flex_blockmask_grid", "flex_blockmask_sparsity",
                     "flex_blockmask_slice", "flex_blockmask_adjust",
                     "flex_status_string", "flex_last_error")
@@ -141,6 +143,11 @@ def load_library():
                                   ctypes.POINTER(flex_block_mask), ctypes.POINTER(flex_block_mask_q), P, P, P, P,
                                   ctypes.c_size_t, P]
     lib.flex_attn_bwd.restype = ctypes.c_int
+    lib.flex_attn_bwd_paged.argtypes = [P, P, P, ctypes.POINTER(flex_kv_pages), P, P, P, I32, I32, I32, I32, I64, I64,
+                                        I32, I64x3, I64x3, I64x3, ctypes.c_float, ctypes.POINTER(flex_score_params),
+                                        ctypes.POINTER(flex_mask_params), ctypes.POINTER(flex_block_mask),
+                                        ctypes.POINTER(flex_block_mask_q), P, P, P, P, ctypes.c_size_t, P]
+    lib.flex_attn_bwd_paged.restype = ctypes.c_int
     BMP = ctypes.POINTER(flex_block_mask)
     lib.flex_blockmask_to_dense.argtypes = [BMP, P, P]
     lib.flex_blockmask_grid.argtypes = [BMP, I32, I32, P, P]
@@ -670,13 +677,44 @@ def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
 
     q, k, v, score, mask, scale and block_mask as for the flex_attn_fwd call
     that returned out and lse; dout like out.  Returns (dq, dk, dv)."""
+    B, Hkv, S = q.shape[0], k.shape[1], k.shape[2]
+    if q.dim() != 4 or k.dim() != 4 or k.shape[0] != B or v.shape[:3] != k.shape[:3]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    return _bwd(q, k, v, None, S, out, dout, lse, block_mask, block_mask_q, score, mask, scale, dq, dk, dv,
+                workspace)
+
+
+def flex_attn_bwd_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                        out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *, S: int, block_mask: BlockMask,
+                        block_mask_q: BlockMaskQ, score: Optional[ScoreSpec] = None,
+                        mask: Optional[MaskSpec] = None, scale: Optional[float] = None,
+                        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                        dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of flex_attn_fwd_paged (C: flex_attn_bwd_paged): pools, page
+    table and S as for that call.  Returns (dq, dk, dv) with dk, dv the
+    gradients of the logical keys and values, (B, Hkv, S, D)."""
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError(f"pool shapes {tuple(k_pool.shape)} / {tuple(v_pool.shape)} differ or are not 4-D")
+    B = q.shape[0]
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.dim() != 2 \
+            or page_table.shape[0] != B:
+        raise ValueError("page_table must be a contiguous int32 (B, max_pages) tensor")
+    _require(page_table, "page_table", q.device, dtype=torch.int32)
+    pages = flex_kv_pages()
+    pages.page_table = page_table.data_ptr()
+    pages.page_size, pages.max_pages, pages.num_pages = k_pool.shape[2], page_table.shape[1], k_pool.shape[0]
+    return _bwd(q, k_pool, v_pool, pages, int(S), out, dout, lse, block_mask, block_mask_q, score, mask, scale, dq,
+                dk, dv, workspace)
+
+
+def _bwd(q, k, v, pages, S, out, dout, lse, block_mask, block_mask_q, score, mask, scale, dq, dk, dv, workspace):
     lib = load_library()
     score = score or ScoreSpec()
     mask = mask or MaskSpec()
     B, Hq, L, D = q.shape
-    Hkv, S = k.shape[1], k.shape[2]
-    if q.dim() != 4 or k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D or v.shape[3] != D:
-        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    Hkv = k.shape[1]
+    if k.shape[3] != D or v.shape[3] != D:
+        raise ValueError(f"head dims differ: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or q.dtype not in DTYPES:
         raise ValueError("q, k, v, out, dout must share a dtype, float32 or bfloat16")
     _require_qkv(q, k, v)
@@ -703,12 +741,16 @@ def flex_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = lambda t: (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     cs, cm = score.to_c(), mask.to_c(L, S)
-    _check(lib.flex_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                             lse.data_ptr(), DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v),
-                             ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.byref(cs),
-                             ctypes.byref(cm), ctypes.byref(cbm), ctypes.byref(cq), dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), workspace.data_ptr(), ws_bytes,
-                             ctypes.c_void_p(_stream_ptr(q.device))))
+    c_scale = ctypes.c_float(0.0 if scale is None else float(scale))
+    tail = (DTYPES[q.dtype], B, Hq, Hkv, L, S, D, st(q), st(k), st(v), c_scale, ctypes.byref(cs), ctypes.byref(cm),
+            ctypes.byref(cbm), ctypes.byref(cq), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            ws_bytes, ctypes.c_void_p(_stream_ptr(q.device)))
+    if pages is None:
+        _check(lib.flex_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), *tail))
+    else:
+        _check(lib.flex_attn_bwd_paged(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(pages), out.data_ptr(),
+                                       dout.data_ptr(), lse.data_ptr(), *tail))
     return dq, dk, dv
 
 

@@ -410,6 +410,43 @@ __device__ __forceinline__ int batch_kv_len(const MaskArgs& m, int b, int S) {
     return m.kv_lens != nullptr ? min(max(scalar_load(m.kv_lens + b), 0), S) : S;
 }
 
+// Where the K/V rows of logical keys [kv0, kv0 + 64) of batch b and K/V
+// head hkv live: the head slice of a contiguous cache, or the page holding
+// them in a paged pool (a page holds whole 64-key tiles).  base points at
+// row 0 of that slice or page, row0 is kv0's row in it and rows bounds the
+// valid rows: keys at or past the batch's filled length S_b read as zeros,
+// whatever the cache holds there.  Page-table entries are clamped into the
+// pool.
+struct KvSlice {
+    const char* kbase;
+    const char* vbase;
+    int row0, rows;
+};
+
+template <typename T>
+__device__ __forceinline__ KvSlice kv_slice(const BwdArgs& a, int b, int hkv, int kv0, int S_b) {
+    const char* k = reinterpret_cast<const char*>(a.k);
+    const char* v = reinterpret_cast<const char*>(a.v);
+    KvSlice sl;
+    if (a.page_table == nullptr) {
+        sl.kbase = k + ((int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh) * (int64_t)sizeof(T);
+        sl.vbase = v + ((int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh) * (int64_t)sizeof(T);
+        sl.row0 = kv0;
+        sl.rows = S_b;
+    } else {
+        // a tile of a wide KV block can start past the last page: its rows
+        // are then all past S and read as zeros
+        const int lp = min(kv0 >> a.page_shift, a.max_pages - 1);
+        int page = scalar_load(a.page_table + (int64_t)b * a.max_pages + lp);
+        page = min(max(page, 0), a.num_pages - 1);
+        sl.kbase = k + ((int64_t)page * a.k_sb + (int64_t)hkv * a.k_sh) * (int64_t)sizeof(T);
+        sl.vbase = v + ((int64_t)page * a.v_sb + (int64_t)hkv * a.v_sh) * (int64_t)sizeof(T);
+        sl.row0 = kv0 - (lp << a.page_shift);
+        sl.rows = min(1 << a.page_shift, S_b - (lp << a.page_shift));
+    }
+    return sl;
+}
+
 // --------------------------------------------------------- key-major pass
 // Tiles of query head hq's Q-side list for KV block kvb (64-row tiles).
 __device__ __forceinline__ int bwd_head_tiles(const BwdArgs& a, int b, int hq, int kvb) {
@@ -478,11 +515,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
     const bool key_ok = key < a.S;
     const bool with_doc = a.mask.uses_doc != 0;
 
-    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    // this workgroup's 64 keys lie in one slice or page; keys past the
+    // batch's filled length load as zeros (and the mask hides them)
+    const KvSlice ksl = kv_slice<T>(a, b, hkv, kv0, S_b);
+    const int krow = ksl.row0 + key - kv0;
     QRegs<T, D> kr, vr;
-    load_q<T, D>(kr, kbase + (int64_t)key * a.k_sr, key_ok, hf);
-    load_q<T, D>(vr, vbase + (int64_t)key * a.v_sr, key_ok, hf);
+    load_q<T, D>(kr, reinterpret_cast<const T*>(ksl.kbase) + (int64_t)krow * a.k_sr, key < S_b, hf);
+    load_q<T, D>(vr, reinterpret_cast<const T*>(ksl.vbase) + (int64_t)krow * a.v_sr, key < S_b, hf);
     const int doc_k = (with_doc && key_ok) ? __ldg(a.mask.doc_id + key) : -3;
 
     f32x16_t dk[D / 32], dv[D / 32];
@@ -772,9 +811,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     const float dsum = row.ok ? a.ws_dsum[srow] : 0.0f;
     const BwdConsts bc = bwd_consts(a, hq);
 
-    const T* kbase = reinterpret_cast<const T*>(a.k) + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-    const T* vbase = reinterpret_cast<const T*>(a.v) + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
-
     const int bm_b = a.Bm > 1 ? b : 0, bm_h = a.Hm > 1 ? hq : 0;
     const int64_t row_id = ((int64_t)bm_b * a.Hm + bm_h) * a.nQB + qb;
     const int n_part = min(max(scalar_load(a.kv_num + row_id), 0), a.nKB);
@@ -823,21 +859,23 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     if constexpr (kDma) {
         const int k_row_bytes = (int)(a.k_sr * (int64_t)sizeof(T));
         const int v_row_bytes = (int)(a.v_sr * (int64_t)sizeof(T));
-        const __amdgpu_buffer_rsrc_t rk = slice_rsrc(kbase, k_row_bytes, a.S);
-        const __amdgpu_buffer_rsrc_t rv = slice_rsrc(vbase, v_row_bytes, a.S);
         const __amdgpu_buffer_rsrc_t rdoc = slice_rsrc(a.mask.doc_id, 4, with_doc ? a.mask.doc_len : 0);
         const int ok_ = dma_lane_offset<D>(k_row_bytes, wave, lane);
         const int ov = dma_lane_offset<D>(v_row_bytes, wave, lane);
         auto issue = [&](auto bi, int kv0) __attribute__((always_inline)) {
             lds_char_t* buf = lds3 + decltype(bi)::value * G::kBufBytes;
+            const KvSlice sl = kv_slice<T>(a, b, hkv, kv0, S_b);
+            const __amdgpu_buffer_rsrc_t rk = slice_rsrc(sl.kbase, k_row_bytes, sl.rows);
+            const __amdgpu_buffer_rsrc_t rv = slice_rsrc(sl.vbase, v_row_bytes, sl.rows);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, ok_,
-                                                         (kv0 + i * dma_rows_per_inst(D)) * k_row_bytes, 0, 0);
+                                                         (sl.row0 + i * dma_rows_per_inst(D)) * k_row_bytes, 0, 0);
 #pragma unroll
             for (int i = 0; i < D / 32; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + G::kTileBytes + (i * 4 + wave) * 1024),
-                                                         16, ov, (kv0 + i * dma_rows_per_inst(D)) * v_row_bytes, 0, 0);
+                                                         16, ov, (sl.row0 + i * dma_rows_per_inst(D)) * v_row_bytes, 0,
+                                                         0);
             if (with_doc && wave == 0) {
                 const int l4 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) * 4;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, l4, kv0 * 4, 0,
@@ -848,10 +886,11 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, char* lds, lds_char_t*
     } else {
         auto issue = [&](auto bi, int kv0) __attribute__((always_inline)) {
             char* buf = lds + decltype(bi)::value * G::kBufBytes;
-            fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(kbase), a.k_sr, kv0, a.S,
-                             tid);
-            fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(vbase),
-                             a.v_sr, kv0, a.S, tid);
+            const KvSlice sl = kv_slice<T>(a, b, hkv, kv0, S_b);
+            fill_tile_f32<D>(reinterpret_cast<float*>(buf), reinterpret_cast<const float*>(sl.kbase), a.k_sr, sl.row0,
+                             sl.rows, tid);
+            fill_tile_f32<D>(reinterpret_cast<float*>(buf + G::kTileBytes), reinterpret_cast<const float*>(sl.vbase),
+                             a.v_sr, sl.row0, sl.rows, tid);
             if (tid < 64) {
                 const int pos = kv0 + tid;
                 int d = -1;

@@ -226,7 +226,9 @@ __device__ __forceinline__ StageOffsets<T, D> stage_offsets(int64_t k_sr, int64_
 // descriptors and byte offsets.  A contiguous cache uses the head slice's
 // descriptors.  A paged cache (PAGED kernels only) sends the logical page
 // kv0 >> page_shift through the batch's page-table row to a physical page of
-// the pool; masks and biases keep using the logical position kv0.
+// the pool; masks and biases keep using the logical position kv0.  As in a
+// contiguous slice, rows at or past the batch's valid length S read as zeros
+// (a partly filled page may hold anything there).
 struct TileAddr {
     __amdgpu_buffer_rsrc_t k, v;
     int ko, vo;
@@ -234,15 +236,17 @@ struct TileAddr {
 
 template <typename T, bool PAGED>
 __device__ __forceinline__ TileAddr tile_addr(const FwdArgs& a, const SliceRsrc& sr, const T* kbase, const T* vbase,
-                                              int b, int kv0) {
+                                              int b, int kv0, int S) {
     TileAddr t{sr.k, sr.v, kv0 * sr.k_row_bytes, kv0 * sr.v_row_bytes};
     if constexpr (PAGED) {
         if (a.page_table != nullptr) {
-            const int lp = kv0 >> a.page_shift;
+            // a tile of a wide KV block can start past the last page: its rows
+            // are then all past S and read as zeros
+            const int lp = min(kv0 >> a.page_shift, a.max_pages - 1);
             int page = scalar_load(a.page_table + (int64_t)b * a.max_pages + lp);
             page = min(max(page, 0), a.num_pages - 1);       // a bad entry reads another page, never outside the pool
             const int in_page = kv0 - (lp << a.page_shift);
-            const int page_rows = 1 << a.page_shift;
+            const int page_rows = min(1 << a.page_shift, S - (lp << a.page_shift));
             t.k = slice_rsrc(kbase + (int64_t)page * a.k_sb, sr.k_row_bytes, page_rows);
             t.v = slice_rsrc(vbase + (int64_t)page * a.v_sb, sr.v_row_bytes, page_rows);
             t.ko = in_page * sr.k_row_bytes;
@@ -904,7 +908,7 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     // K and V instructions per wave and tile (wave 0 adds one doc-id load).
     constexpr int kPerTile = 2 * DmaPlan<D>::kInsts;
     auto issue = [&](char* buf, int kv0) {
-        const TileAddr ta = tile_addr<__bf16, PAGED>(a, sr, kbase, vbase, b, kv0);
+        const TileAddr ta = tile_addr<__bf16, PAGED>(a, sr, kbase, vbase, b, kv0, S);
 #pragma unroll
         for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ta.k, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
@@ -1021,7 +1025,7 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
     Stage<T, D> stage;
     bool masked;
     int kv0 = tile_kv0(tile_lo, masked);
-    stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, kv0), sr, kv0, with_doc, tid);
+    stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, kv0, S), sr, kv0, with_doc, tid);
     stage_store<T, D>(stage, lds, with_doc, tid);
     __syncthreads();
     for (int t = tile_lo; t < tile_hi; ++t) {
@@ -1031,7 +1035,7 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
         const bool has_next = t + 1 < tile_hi;
         if (has_next) {
             next_kv0 = tile_kv0(t + 1, next_masked);
-            stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, next_kv0), sr, next_kv0, with_doc,
+            stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, next_kv0, S), sr, next_kv0, with_doc,
                              tid);
         }
         const char* cur = lds + buf * G::kBufBytes;

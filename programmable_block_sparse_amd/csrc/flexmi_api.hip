@@ -331,6 +331,27 @@ flex_status flex_attn_fwd(const void* q, const void* k, const void* v, int32_t d
                              bm, out, lse, nullptr, workspace, workspace_bytes, stream);
 }
 
+// Page geometry of a paged K/V pool (both passes); page_shift = log2(page_size).
+static flex_status check_pages(const flex_kv_pages* pages, int32_t dtype, int32_t B, int64_t S, int32_t D,
+                               const int64_t k_strides[3], const int64_t v_strides[3], int* page_shift) {
+    if (!pages->page_table) return fail(FLEX_ERR_NULL, "page_table must not be NULL");
+    if (reinterpret_cast<uintptr_t>(pages->page_table) & 3u)
+        return fail(FLEX_ERR_LAYOUT, "page_table must be 4-byte aligned");
+    const int32_t ps = pages->page_size;
+    if (ps < 64 || ps > (1 << 20) || (ps & (ps - 1)))
+        return fail(FLEX_ERR_PARAM, "page_size must be a power of two in [64, 2^20] (got %d)", ps);
+    *page_shift = 0;
+    while ((1 << *page_shift) < ps) ++*page_shift;
+    if (pages->num_pages < 1 || pages->max_pages < 1 || (int64_t)pages->max_pages * ps < S)
+        return fail(FLEX_ERR_PARAM, "max_pages * page_size must cover S and num_pages be >= 1");
+    if ((int64_t)B * pages->max_pages >= (int64_t(1) << 31)) return fail(FLEX_ERR_PARAM, "page table too large");
+    const int64_t elem = dtype == FLEX_BF16 ? 2 : 4;
+    if ((int64_t)ps * std::max(k_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31) ||
+        (int64_t)ps * std::max(v_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31))
+        return fail(FLEX_ERR_UNSUPPORTED, "one page of one head must stay below 2 GiB");
+    return FLEX_OK;
+}
+
 static flex_status fwd_common(const void* q, const void* k, const void* v, int32_t dtype, int32_t B, int32_t Hq,
                               int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
                               const int64_t k_strides[3], const int64_t v_strides[3], float scale,
@@ -341,22 +362,8 @@ static flex_status fwd_common(const void* q, const void* k, const void* v, int32
                                   bm, out, lse))
         return s;
     int page_shift = 0;
-    if (pages) {
-        if (!pages->page_table) return fail(FLEX_ERR_NULL, "page_table must not be NULL");
-        if (reinterpret_cast<uintptr_t>(pages->page_table) & 3u)
-            return fail(FLEX_ERR_LAYOUT, "page_table must be 4-byte aligned");
-        const int32_t ps = pages->page_size;
-        if (ps < 64 || ps > (1 << 20) || (ps & (ps - 1)))
-            return fail(FLEX_ERR_PARAM, "page_size must be a power of two in [64, 2^20] (got %d)", ps);
-        while ((1 << page_shift) < ps) ++page_shift;
-        if (pages->num_pages < 1 || pages->max_pages < 1 || (int64_t)pages->max_pages * ps < S)
-            return fail(FLEX_ERR_PARAM, "max_pages * page_size must cover S and num_pages be >= 1");
-        if ((int64_t)B * pages->max_pages >= (int64_t(1) << 31)) return fail(FLEX_ERR_PARAM, "page table too large");
-        const int64_t elem = dtype == FLEX_BF16 ? 2 : 4;
-        if ((int64_t)ps * std::max(k_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31) ||
-            (int64_t)ps * std::max(v_strides[2], (int64_t)D) * elem >= (int64_t(1) << 31))
-            return fail(FLEX_ERR_UNSUPPORTED, "one page of one head must stay below 2 GiB");
-    }
+    if (pages)
+        if (flex_status s = check_pages(pages, dtype, B, S, D, k_strides, v_strides, &page_shift)) return s;
     if (!std::isfinite(scale)) return fail(FLEX_ERR_PARAM, "scale must be finite");
     if (max_scores && (reinterpret_cast<uintptr_t>(max_scores) & 3u))
         return fail(FLEX_ERR_LAYOUT, "max_scores must be 4-byte aligned");
@@ -577,16 +584,19 @@ size_t flex_attn_bwd_workspace_bytes(int32_t dtype, int32_t B, int32_t Hq, int32
                                     bm->num_kv_blocks);
 }
 
-flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                          const float* lse, int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
-                          int32_t D, const int64_t q_strides[3], const int64_t k_strides[3],
-                          const int64_t v_strides[3], float scale, const flex_score_params* score,
-                          const flex_mask_params* mask, const flex_block_mask* bm, const flex_block_mask_q* bmq,
-                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-    g_last_error.clear();
+static flex_status bwd_common(const void* q, const void* k, const void* v, const flex_kv_pages* pages,
+                              const void* out, const void* dout, const float* lse, int32_t dtype, int32_t B,
+                              int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                              const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                              const flex_score_params* score, const flex_mask_params* mask, const flex_block_mask* bm,
+                              const flex_block_mask_q* bmq, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, void* stream) {
     if (flex_status s = check_fwd(q, k, v, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides, score, mask,
                                   bm, out, lse))
         return s;
+    int page_shift = 0;
+    if (pages)
+        if (flex_status s = check_pages(pages, dtype, B, S, D, k_strides, v_strides, &page_shift)) return s;
     if (!dout || !lse || !dq || !dk || !dv) return fail(FLEX_ERR_NULL, "dout, lse, dq, dk and dv must not be NULL");
     if (!bmq) return fail(FLEX_ERR_NULL, "bmq must not be NULL");
     if (!bmq->q_num_blocks || !bmq->q_indices || !bmq->full_q_num_blocks || !bmq->full_q_indices)
@@ -656,10 +666,38 @@ flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const voi
     a.nKB = bm->num_kv_blocks;
     a.q_block = bm->q_block;
     a.kv_block = bm->kv_block;
+    a.page_table = pages ? pages->page_table : nullptr;
+    a.page_shift = page_shift;
+    a.max_pages = pages ? pages->max_pages : 0;
+    a.num_pages = pages ? pages->num_pages : 0;
     (void)hipGetLastError();
     hipError_t e = launch_attn_bwd(dtype, D, a, as_stream(stream));
     if (e != hipSuccess) return fail(FLEX_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return FLEX_OK;
+}
+
+flex_status flex_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, int32_t dtype, int32_t B, int32_t Hq, int32_t Hkv, int64_t L, int64_t S,
+                          int32_t D, const int64_t q_strides[3], const int64_t k_strides[3],
+                          const int64_t v_strides[3], float scale, const flex_score_params* score,
+                          const flex_mask_params* mask, const flex_block_mask* bm, const flex_block_mask_q* bmq,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    return bwd_common(q, k, v, nullptr, out, dout, lse, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides,
+                      scale, score, mask, bm, bmq, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+flex_status flex_attn_bwd_paged(const void* q, const void* k, const void* v, const flex_kv_pages* pages,
+                                const void* out, const void* dout, const float* lse, int32_t dtype, int32_t B,
+                                int32_t Hq, int32_t Hkv, int64_t L, int64_t S, int32_t D, const int64_t q_strides[3],
+                                const int64_t k_strides[3], const int64_t v_strides[3], float scale,
+                                const flex_score_params* score, const flex_mask_params* mask,
+                                const flex_block_mask* bm, const flex_block_mask_q* bmq, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!pages) return fail(FLEX_ERR_NULL, "pages must not be NULL");
+    return bwd_common(q, k, v, pages, out, dout, lse, dtype, B, Hq, Hkv, L, S, D, q_strides, k_strides, v_strides,
+                      scale, score, mask, bm, bmq, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 flex_status flex_blockmask_to_dense(const flex_block_mask* bm, int32_t* dense, void* stream) {

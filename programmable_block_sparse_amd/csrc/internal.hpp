@@ -188,6 +188,11 @@ struct BwdArgs {
     const int* fq_num;
     const int* fq_idx;
     int Bm, Hm, nQB, nKB, q_block, kv_block;
+    // paged K/V (NULL page_table: contiguous): k, v are pools, k_sb / v_sb
+    // the page strides; logical key j of batch b is row j % page_size of
+    // page page_table[b * max_pages + j / page_size]
+    const int* page_table;
+    int page_shift, max_pages, num_pages;
 };
 
 // Q-side tiles one workgroup of the key-major pass takes before a column is

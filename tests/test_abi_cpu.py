@@ -395,6 +395,30 @@ def test_paged_forward_rejects(lib):
         assert call(pg) == code, (field, bad, pbs.flex_last_error())
 
 
+def test_paged_backward_rejects(lib):
+    """flex_attn_bwd_paged: the backward's checks plus the page geometry."""
+    f = Bwd(L=128, S=1000, qb=64)
+    a3 = lambda x: (ctypes.c_int64 * 3)(*x)
+    ref = lambda x: None if x is None else ctypes.byref(x)
+
+    def call(pg, bmq=f.bmq):
+        return lib.flex_attn_bwd_paged(f.q, f.k, f.v, ref(pg), f.out, f.dout, f.lse, f.dtype, f.B, f.Hq, f.Hkv, f.L,
+                                       f.S, f.D, a3(f.qs), a3([64 * 64 * 2, 64 * 64, 64]),
+                                       a3([64 * 64 * 2, 64 * 64, 64]), ctypes.c_float(0.0), ref(f.score),
+                                       ref(f.mask), ref(f.bm), ref(bmq), f.dq, f.dk, f.dv, f.ws, f.ws_bytes, None)
+    pages = pbs.flex_kv_pages()
+    pages.page_table, pages.page_size, pages.max_pages, pages.num_pages = FAKE, 64, 16, 40
+    assert call(pages) in (OK, HIP), pbs.flex_last_error()
+    assert call(None) == NULL
+    assert call(pages, bmq=None) == NULL
+    for field, bad, code in (("page_size", 48, PARAM), ("page_size", 32, PARAM), ("max_pages", 15, PARAM),
+                             ("num_pages", 0, PARAM), ("page_table", None, NULL), ("page_table", FAKE + 2, LAYOUT)):
+        pg = pbs.flex_kv_pages()
+        pg.page_table, pg.page_size, pg.max_pages, pg.num_pages = FAKE, 64, 16, 40
+        setattr(pg, field, bad)
+        assert call(pg) == code, (field, bad, pbs.flex_last_error())
+
+
 def test_per_batch_arrays_need_per_batch_block_mask(lib):
     f = Fwd()
     f.mask.kv_lens = FAKE

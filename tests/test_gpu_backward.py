@@ -295,6 +295,56 @@ def test_bwd_per_batch_long_columns(dev):
                       split_cols=True, what="per-batch split columns")
 
 
+@pytest.mark.parametrize("dtype,D,page,kb", [("bf16", 64, 64, 64), ("bf16", 128, 128, 64), ("f32", 64, 64, 64),
+                                             ("f32", 128, 256, 64), ("bf16", 64, 64, 128)])
+def test_bwd_paged_cache(dev, dtype, D, page, kb):
+    """Backward over a paged cache: K/V scattered into a shuffled pool whose
+    unfilled rows hold finite junk.  Fed the same out and lse, the paged
+    backward must give the contiguous backward's gradients bit for bit (same
+    arithmetic, other addresses), and both match the oracle.  With 128-key
+    blocks over 700 keys the last block's second tile starts past the last
+    page."""
+    B, Hq, Hkv, L, S = 3, 4, 2, 150, 700
+    offs, lens = [S - L, 300, 40], [S, 300 + L, 190]
+    rng = np.random.default_rng(500 + D + page)
+    q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    do = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
+    score = dict(kind="softcap_alibi", cap=20.0, alibi_m=8.0)
+    spec = pbs.MaskSpec(kind="causal", q_offset=0, q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev))
+    bm = pbs.flex_blockmask_build(spec, L, S, 64, kb, B=B, device=dev)
+    bmq = pbs.flex_blockmask_transpose(bm)
+    sspec = pbs.ScoreSpec(**score)
+    n_log = -(-S // page)
+    n_phys = B * n_log + 3
+    table = rng.permutation(n_phys)[:B * n_log].reshape(B, n_log).astype(np.int32)
+    pool_k = rng.uniform(-50, 50, (n_phys, Hkv, page, D)).astype(np.float32)   # junk where nothing was written
+    pool_v = rng.uniform(-50, 50, (n_phys, Hkv, page, D)).astype(np.float32)
+    for b in range(B):
+        for p in range(-(-lens[b] // page)):
+            n = min(page, lens[b] - p * page)
+            pool_k[table[b, p], :, :n] = k[b, :, p * page:p * page + n]
+            pool_v[table[b, p], :, :n] = v[b, :, p * page:p * page + n]
+    qt, kt, vt, dot = (_tensor(x, dtype, dev) for x in (q, k, v, do))
+    pk, pv = _tensor(pool_k, dtype, dev), _tensor(pool_v, dtype, dev)
+    tt = torch.from_numpy(table).to(dev)
+    out, lse = pbs.flex_attn_fwd(qt, kt, vt, block_mask=bm, score=sspec, mask=spec)
+    out_p, lse_p, _ = pbs.flex_attn_fwd_paged(qt, pk, pv, tt, S=S, block_mask=bm, score=sspec, mask=spec)
+    g_c = pbs.flex_attn_bwd(qt, kt, vt, out, dot, lse, block_mask=bm, block_mask_q=bmq, score=sspec, mask=spec)
+    g_p = pbs.flex_attn_bwd_paged(qt, pk, pv, tt, out, dot, lse, S=S, block_mask=bm, block_mask_q=bmq, score=sspec,
+                                  mask=spec)
+    torch.cuda.synchronize()
+    what = f"paged bwd {dtype} D={D} page={page} kv_block={kb}"
+    assert torch.equal(out_p, out) and torch.equal(lse_p, lse), f"{what}: paged forward differs from contiguous"
+    for name, a_, c_ in zip(("dq", "dk", "dv"), g_p, g_c):
+        assert torch.equal(a_, c_), f"{what}: {name} differs from the contiguous backward"
+    sc = oracle_default_scale(D)
+    ref = attention_backward(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), _widen(do, dtype), scale=sc,
+                             score=ScoreMod(**score), mask=MaskMod("causal"), q_offset=offs, kv_len=lens)
+    assert_grads_close(g_p, ref, dtype, what)
+
+
 @pytest.mark.parametrize("D,L,sinks", [(64, 300, 0), (128, 300, 0), (128, 1100, 4)])
 def test_bwd_deterministic(dev, D, L, sinks):
     """Two runs give bitwise equal gradients: every dq row and every dk, dv

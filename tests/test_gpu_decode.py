@@ -122,3 +122,11 @@ def test_circular_buffer(dev):
     run(dev, seed=9, dtype="bf16", B=2, Hq=8, Hkv=2, L=16, S=1000, D=128, qb=16, kb=64,
         score=dict(kind="softcap", cap=50.0), kind="causal_window_sinks", window=150, sinks=0,
         offs=[984, 700], lens=[1000, 716], page_size=64, ring_pages=4, what="ring of 4 pages")
+
+
+def test_paged_cache_wide_kv_blocks(dev):
+    # 128-key blocks over a 900-key cache of 64-key pages: the last block's
+    # second tile starts past the last page (its rows read as zeros)
+    run(dev, seed=77, dtype="bf16", B=2, Hq=4, Hkv=2, L=120, S=900, D=64, qb=64, kb=128,
+        score=dict(kind="softcap", cap=30.0), kind="causal", offs=[780, 300], lens=[900, 420], page_size=64,
+        what="paged kv_block 128")
