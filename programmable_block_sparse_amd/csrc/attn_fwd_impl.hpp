@@ -436,7 +436,8 @@ __device__ __forceinline__ void pack_p(bf16x8_t (&pb)[2], const float (&p)[16]) 
 }
 
 // acc plus the sum of the rounded probabilities (two per v_dot2 against a
-// pair of ones, in two independent chains).
+// pair of ones; SPLIT: in two independent chains, one register more).
+template <bool SPLIT>
 __device__ __forceinline__ float sum_packed(const bf16x8_t (&pb)[2], float acc) {
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float part[2] = {acc, 0.0f};
@@ -445,9 +446,10 @@ __device__ __forceinline__ float sum_packed(const bf16x8_t (&pb)[2], float acc) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bf16x2_t pair = {pb[t][2 * e], pb[t][2 * e + 1]};
-            part[t] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[t], false);
+            float& dst = SPLIT ? part[t] : part[0];
+            dst = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, dst, false);
         }
-    return part[0] + part[1];
+    return SPLIT ? part[0] + part[1] : part[0];
 }
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -790,7 +792,7 @@ __device__ __forceinline__ void tile_update(const f32x16_t& s, const char* __res
         } else {
             bf16x8_t pb[2];
             pack_p(pb, z);
-            st.lr = sum_packed(pb, st.lr);
+            st.lr = sum_packed<CUBIC_FIRST>(pb, st.lr);
             pv_bf16<D>(o, pb, reinterpret_cast<const char*>(Vs), la, kb2_lds);
         }
     }
@@ -1162,10 +1164,11 @@ __device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, i
 // waves hide MFMA and LDS latency behind each other's VALU work), otherwise
 // as many as the registers of the wider tiles allow.  The extended kernels
 // (mask programs, max_scores) at head dim 64 need more than the 168 registers
-// of three waves and would spill, so they take two.
-template <typename T, int D, bool KSPLIT, bool EXT> struct PrefillOccupancy {
+// of three waves and would spill, so they take two; the key-split paged ones
+// need more than the 128 of four and take three.
+template <typename T, int D, bool KSPLIT, bool EXT, bool PAGED = false> struct PrefillOccupancy {
     static constexpr int value =
-        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 2 : 4) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
+        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 2 : (PAGED ? 3 : 4)) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
 };
 
 
@@ -1224,7 +1227,7 @@ static_assert(kLongestFirstMaxBlocks <= kThreads, "one Q block per thread when o
 // workgroup (short critical path when a few Q blocks hold most of the work);
 // otherwise a part is 128 rows, one 32-row group per wave, both key halves.
 template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, bool PAGED>
-__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT>::value)) void attn_fwd_prefill(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT, PAGED>::value)) void attn_fwd_prefill(FwdArgs a) {
     using G = Tiles<T, D>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::kBufBytes];
     constexpr int kRows = KSPLIT ? 64 : 128;
