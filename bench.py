@@ -22,7 +22,8 @@ key-major and query-major passes) against its 10*D per cell.
 
 With --paged PAGE_SIZE the K/V caches are first scattered into a pool of
 pages in a seeded random order and the forward reads them through the page
-table (flex_attn_fwd_paged); everything else is the same.
+table (flex_attn_fwd_paged; with --pass bwd also the backward,
+flex_attn_bwd_paged); everything else is the same.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--paged N]
 """
@@ -53,7 +54,7 @@ def parse():
                    help="fwd: the forward hot path (default); bwd: forward + backward training pass")
     p.add_argument("--paged", type=int, default=0, metavar="PAGE_SIZE",
                    help="keep K/V in a paged pool of PAGE_SIZE-key pages (seeded random page order) and run the "
-                        "paged forward")
+                        "paged forward (and, with --pass bwd, the paged backward)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch from Python each step instead of replaying a HIP graph")
     p.add_argument("--cpu-sample-heads", type=int, default=0, help="0 = automatic (about 10 s of oracle work)")
@@ -189,25 +190,8 @@ def main():
         pbs.flex_attn_fwd(q, k, v, block_mask=block_mask, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws)
 
     if args.paged:
-        # a pool of pages holding every batch's cache, in a seeded random page
-        # order; logical page p of batch b sits in pool page table[b, p]
-        ps = args.paged
-        n_log = -(-w.S // ps)
-        perm = torch.from_numpy(np.random.Generator(np.random.PCG64(w.seed + 77)).permutation(w.B * n_log)
-                                .astype(np.int64)).to(dev)
-        table = perm.view(w.B, n_log).to(torch.int32).contiguous()
-
-        def to_pool(x):
-            xp = torch.zeros((w.B, w.Hkv, n_log * ps, w.D), dtype=x.dtype, device=dev)
-            xp[:, :, :w.S] = x
-            pages = xp.view(w.B, w.Hkv, n_log, ps, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * n_log, w.Hkv, ps, w.D)
-            pool = torch.empty_like(pages)
-            pool[perm] = pages
-            return pool
-        k_pool, v_pool = to_pool(k), to_pool(v)
+        k_pool, v_pool, table = paged_pools(w, k, v, args.paged, dev)
         del k, v
-        torch.cuda.synchronize()
-        print(f"bench: paged K/V, {w.B * n_log} pages of {ps} keys", file=sys.stderr, flush=True)
 
         def attend(block_mask):
             pbs.flex_attn_fwd_paged(q, k_pool, v_pool, table, S=w.S, block_mask=block_mask, score=sspec, mask=mspec,
@@ -389,6 +373,29 @@ def time_units(units, args, dev, windows=5, min_calls=50, warm_ms=100.0):
     return out
 
 
+def paged_pools(w, k, v, ps, dev):
+    """K/V scattered into pools of ps-key pages in a seeded random page order:
+    logical page p of batch b sits in pool page table[b, p].  Returns the two
+    pools and the int32 page table."""
+    import torch
+    n_log = -(-w.S // ps)
+    perm = torch.from_numpy(np.random.Generator(np.random.PCG64(w.seed + 77)).permutation(w.B * n_log)
+                            .astype(np.int64)).to(dev)
+    table = perm.view(w.B, n_log).to(torch.int32).contiguous()
+
+    def to_pool(x):
+        xp = torch.zeros((w.B, w.Hkv, n_log * ps, w.D), dtype=x.dtype, device=dev)
+        xp[:, :, :w.S] = x
+        pages = xp.view(w.B, w.Hkv, n_log, ps, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * n_log, w.Hkv, ps, w.D)
+        pool = torch.empty_like(pages)
+        pool[perm] = pages
+        return pool
+    pools = to_pool(k), to_pool(v)
+    torch.cuda.synchronize()
+    print(f"bench: paged K/V, {w.B * n_log} pages of {ps} keys", file=sys.stderr, flush=True)
+    return pools[0], pools[1], table
+
+
 def bwd_kernel_names(w) -> str:
     """Kernels of one backward call: the two major passes share one launch
     under GQA at head dim 128 (bf16, element-rule masks); long Q-side columns
@@ -441,16 +448,34 @@ def main_bwd(args):
     bm_step = pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, device=dev)
     bmq_step = pbs.flex_blockmask_transpose(bm_step)
 
+    def fwd_call(block_mask):
+        pbs.flex_attn_fwd(q, k, v, block_mask=block_mask, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws_f)
+
+    def bwd_call(block_mask, block_mask_q):
+        pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=block_mask, block_mask_q=block_mask_q, score=sspec,
+                          mask=mspec, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+
+    if args.paged:
+        k_pool, v_pool, table = paged_pools(w, k, v, args.paged, dev)
+        del k, v
+
+        def fwd_call(block_mask):
+            pbs.flex_attn_fwd_paged(q, k_pool, v_pool, table, S=w.S, block_mask=block_mask, score=sspec, mask=mspec,
+                                    out=out, lse=lse, workspace=ws_f)
+
+        def bwd_call(block_mask, block_mask_q):
+            pbs.flex_attn_bwd_paged(q, k_pool, v_pool, table, out, dout, lse, S=w.S, block_mask=block_mask,
+                                    block_mask_q=block_mask_q, score=sspec, mask=mspec, dq=dq, dk=dk, dv=dv,
+                                    workspace=ws_b)
+
     def bwd():
-        pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=bm, block_mask_q=bmq, score=sspec, mask=mspec,
-                          dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        bwd_call(bm, bmq)
 
     def step():
         pbs.flex_blockmask_build(mspec, w.L, w.S, w.q_block, w.kv_block, out=bm_step)
         pbs.flex_blockmask_transpose(bm_step, out=bmq_step)
-        pbs.flex_attn_fwd(q, k, v, block_mask=bm_step, score=sspec, mask=mspec, out=out, lse=lse, workspace=ws_f)
-        pbs.flex_attn_bwd(q, k, v, out, dout, lse, block_mask=bm_step, block_mask_q=bmq_step, score=sspec,
-                          mask=mspec, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        fwd_call(bm_step)
+        bwd_call(bm_step, bmq_step)
 
     def transpose_only():
         pbs.flex_blockmask_transpose(bm_step, out=bmq_step)
@@ -472,7 +497,7 @@ def main_bwd(args):
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     bwd_tflops = bwd_flops / (ms_bwd * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": bwd_tflops, "peak": peak, "unit": "TFLOP/s", "frac": bwd_tflops / peak,
-            "traffic": measured_traffic(w.name, backward=True), "kernel": bwd_kernel_names(w),
+            "traffic": None if args.paged else measured_traffic(w.name, backward=True), "kernel": bwd_kernel_names(w),
             "algorithmic_per_launch": bwd_flops}
     result = {
         "metric": "flex fwd+bwd TFLOP/s (visited-block FLOPs: 4*D fwd + 10*D bwd per cell)",
@@ -480,13 +505,14 @@ def main_bwd(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs and upstream gradient, PCG64 seed %d)" % w.seed,
-        "config": {"workload": w.name + "_train", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S,
-                   "D": w.D, "mask": w.mask, "score": w.score, "cap": w.cap, "window": w.window,
-                   "sinks": w.sinks, "q_block": w.q_block, "kv_block": w.kv_block, "q_offset": w.q_offset},
+        "config": {"workload": w.name + "_train" + (f"_paged{args.paged}" if args.paged else ""), "B": w.B,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "S": w.S, "D": w.D, "mask": w.mask, "score": w.score,
+                   "cap": w.cap, "window": w.window, "sinks": w.sinks, "q_block": w.q_block,
+                   "kv_block": w.kv_block, "q_offset": w.q_offset, "page_size": args.paged or None},
         "roofline": roof, "bwd_ms": ms_bwd, "transpose_ms": ms_tr, "launch_mode": mode, "timing": tm,
         "bwd_tflops_visited": bwd_tflops, "fwd_visited_flops": fwd_flops, "bwd_visited_flops": bwd_flops,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.paged:
         result.update(cpu_baseline_bwd(args, w, inp, up, (dq, dk, dv), bwd_flops))
     print(json.dumps(result), flush=True)
 

@@ -130,3 +130,66 @@ def test_paged_cache_wide_kv_blocks(dev):
     run(dev, seed=77, dtype="bf16", B=2, Hq=4, Hkv=2, L=120, S=900, D=64, qb=64, kb=128,
         score=dict(kind="softcap", cap=30.0), kind="causal", offs=[780, 300], lens=[900, 420], page_size=64,
         what="paged kv_block 128")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_unfilled_cache_rows_are_never_read(dev, paged):
+    """Cache rows at or past a batch's filled length hold NaN: the forward and
+    the backward must give the same bits as with zeros there (those rows load
+    as zeros, so no 0 * NaN reaches a product), on the split-KV decode path and
+    the prefill path, contiguous and paged."""
+    B, Hq, Hkv, S, D, page = 2, 8, 2, 1000, 64, 64
+    lens = [700, 333]
+    rng = np.random.default_rng(91)
+    n_log = -(-S // page)
+    table = rng.permutation(B * n_log + 2)[:B * n_log].reshape(B, n_log).astype(np.int32)
+    tt = torch.from_numpy(table).to(dev)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+
+    def caches(fill):
+        kc, vc = k.copy(), v.copy()
+        for b, n in enumerate(lens):
+            kc[b, :, n:] = fill
+            vc[b, :, n:] = fill
+        if not paged:
+            return _t(kc, "bf16", dev), _t(vc, "bf16", dev)
+        pk = np.full((B * n_log + 2, Hkv, page, D), fill, np.float32)
+        pv = np.full_like(pk, fill)
+        kp = np.full((B, Hkv, n_log * page, D), fill, np.float32)
+        vp = np.full_like(kp, fill)
+        kp[:, :, :S], vp[:, :, :S] = kc, vc
+        for b in range(B):
+            for p in range(n_log):
+                pk[table[b, p]] = kp[b, :, p * page:(p + 1) * page]
+                pv[table[b, p]] = vp[b, :, p * page:(p + 1) * page]
+        return _t(pk, "bf16", dev), _t(pv, "bf16", dev)
+
+    for L, qb in ((16, 16), (130, 64)):
+        offs = [n - L for n in lens]
+        q = _t(rng.standard_normal((B, Hq, L, D), dtype=np.float32), "bf16", dev)
+        do = _t(rng.standard_normal((B, Hq, L, D), dtype=np.float32), "bf16", dev)
+        spec = pbs.MaskSpec("causal", q_offset=0, q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev))
+        score = pbs.ScoreSpec(kind="softcap", cap=30.0)
+        bm = pbs.flex_blockmask_build(spec, L, S, qb, 64, B=B, device=dev)
+        res = []
+        for fill in (0.0, np.nan):
+            kc, vc = caches(fill)
+            if paged:
+                out, lse, _ = pbs.flex_attn_fwd_paged(q, kc, vc, tt, S=S, block_mask=bm, score=score, mask=spec)
+            else:
+                out, lse = pbs.flex_attn_fwd(q, kc, vc, block_mask=bm, score=score, mask=spec)
+            grads = ()
+            if qb == 64:
+                bmq = pbs.flex_blockmask_transpose(bm)
+                if paged:
+                    grads = pbs.flex_attn_bwd_paged(q, kc, vc, tt, out, do, lse, S=S, block_mask=bm, block_mask_q=bmq,
+                                                    score=score, mask=spec)
+                else:
+                    grads = pbs.flex_attn_bwd(q, kc, vc, out, do, lse, block_mask=bm, block_mask_q=bmq, score=score,
+                                              mask=spec)
+            torch.cuda.synchronize()
+            res.append((out, lse) + tuple(grads))
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), res[0], res[1]):
+            assert not torch.isnan(b).any(), f"L={L} paged={paged}: NaN in {name}"
+            assert torch.equal(a, b), f"L={L} paged={paged}: {name} depends on the unfilled rows"
