@@ -146,7 +146,8 @@ typedef enum {
  *   doc_id    DOC_CAUSAL and the DOC predicate: device int32[doc_len],
  *             document index per position
  *   doc_len   must then cover every key and query position, i.e.
- *             doc_len >= max(S, q_offset + L) with q_offset >= 0
+ *             doc_len >= max(S, q_offset + L) with q_offset >= 0, and stay
+ *             below 2^29
  *   n_clauses, clause   PROGRAM: 1 <= n_clauses <= FLEX_MAX_CLAUSES clauses,
  *             all of which must hold
  *   q_offsets optional device int32[B]: the logical position of query row 0

@@ -648,7 +648,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
                     // rows whose position is outside doc_id read 0 (out of
                     // range); mask_bits_keys hides them
                     const int pos = q0 + q_off + l4 / 4;
-                    const int voff = (pos >= 0 && pos < a.mask.doc_len) ? pos * 4 : 0x7ffffff0;
+                    const int voff = (pos >= 0 && pos < a.mask.doc_len) ? pos * 4 : 0x7ffffff0;   // doc_len < 2^29
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rdoc, (lds_void_t*)(buf + G::kDocOffset), 4, voff, 0, 0,
                                                              0);
                 }

@@ -110,9 +110,12 @@ flex_status check_mask(const flex_mask_params* m, int64_t L, int64_t S) {
         if (m->doc_id == nullptr) return fail(FLEX_ERR_NULL, "a document mask needs doc_id");
         if (m->q_offset < 0 && !m->q_offsets) return fail(FLEX_ERR_PARAM, "a document mask needs q_offset >= 0");
         const int64_t need = std::max<int64_t>(S, m->q_offset + L);
-        if (m->doc_len < need || m->doc_len >= kMaxLen)
+        if (m->doc_len < need)
             return fail(FLEX_ERR_PARAM, "doc_len %lld must cover max(S, q_offset + L) = %lld",
                         (long long)m->doc_len, (long long)need);
+        // the kernels address doc_id through 2 GiB buffer descriptors
+        if (m->doc_len >= (int64_t(1) << 29))
+            return fail(FLEX_ERR_PARAM, "doc_len %lld must stay below 2^29", (long long)m->doc_len);
         if (reinterpret_cast<uintptr_t>(m->doc_id) & 3u)
             return fail(FLEX_ERR_LAYOUT, "doc_id must be 4-byte aligned");
     }

@@ -102,6 +102,7 @@ def test_builder_rejects(lib):
     assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S - 1), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S, q_offset=-1), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=S, q_offset=5), L, S, _bm(L, S, 64, 64)) == PARAM
+    assert build(lib, _mask("doc_causal", doc=FAKE, doc_len=1 << 29), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask(q_offset=1 << 30), L, S, _bm(L, S, 64, 64)) == PARAM
     assert build(lib, _mask(), 64, 64 * 70000, _bm(64, 64 * 70000, 64, 64)) == UNSUPPORTED
     assert build(lib, _mask(), 70000, 64, _bm(70000, 64, 1, 64)) == UNSUPPORTED
