@@ -222,9 +222,16 @@ __device__ __forceinline__ StageOffsets<T, D> stage_offsets(int64_t k_sr, int64_
     return so;
 }
 
+// K/V layouts a kernel is compiled for: contiguous (B, Hkv, S, D) caches;
+// contiguous caches with per-batch query offsets and filled lengths; paged
+// pools (with or without the per-batch arrays).  Each has its own kernels, so
+// a paged kernel keeps no contiguous descriptors live and a contiguous one no
+// page-table state.
+constexpr int kKvContig = 0, kKvPerBatch = 1, kKvPaged = 2;
+
 // Where the K and V rows of the tile starting at logical key kv0 live: buffer
 // descriptors and byte offsets.  A contiguous cache uses the head slice's
-// descriptors.  A paged cache (PAGED kernels only) sends the logical page
+// descriptors.  A paged cache (kKvPaged kernels) sends the logical page
 // kv0 >> page_shift through the batch's page-table row to a physical page of
 // the pool; masks and biases keep using the logical position kv0.  As in a
 // contiguous slice, rows at or past the batch's valid length S read as zeros
@@ -234,26 +241,22 @@ struct TileAddr {
     int ko, vo;
 };
 
-template <typename T, bool PAGED>
+template <typename T, int KVL>
 __device__ __forceinline__ TileAddr tile_addr(const FwdArgs& a, const SliceRsrc& sr, const T* kbase, const T* vbase,
                                               int b, int kv0, int S) {
-    TileAddr t{sr.k, sr.v, kv0 * sr.k_row_bytes, kv0 * sr.v_row_bytes};
-    if constexpr (PAGED) {
-        if (a.page_table != nullptr) {
-            // a tile of a wide KV block can start past the last page: its rows
-            // are then all past S and read as zeros
-            const int lp = min(kv0 >> a.page_shift, a.max_pages - 1);
-            int page = scalar_load(a.page_table + (int64_t)b * a.max_pages + lp);
-            page = min(max(page, 0), a.num_pages - 1);       // a bad entry reads another page, never outside the pool
-            const int in_page = kv0 - (lp << a.page_shift);
-            const int page_rows = min(1 << a.page_shift, S - (lp << a.page_shift));
-            t.k = slice_rsrc(kbase + (int64_t)page * a.k_sb, sr.k_row_bytes, page_rows);
-            t.v = slice_rsrc(vbase + (int64_t)page * a.v_sb, sr.v_row_bytes, page_rows);
-            t.ko = in_page * sr.k_row_bytes;
-            t.vo = in_page * sr.v_row_bytes;
-        }
+    if constexpr (KVL == kKvPaged) {
+        // a tile of a wide KV block can start past the last page: its rows
+        // are then all past S and read as zeros
+        const int lp = min(kv0 >> a.page_shift, a.max_pages - 1);
+        int page = scalar_load(a.page_table + (int64_t)b * a.max_pages + lp);
+        page = min(max(page, 0), a.num_pages - 1);       // a bad entry reads another page, never outside the pool
+        const int in_page = kv0 - (lp << a.page_shift);
+        const int page_rows = min(1 << a.page_shift, S - (lp << a.page_shift));
+        return TileAddr{slice_rsrc(kbase + (int64_t)page * a.k_sb, sr.k_row_bytes, page_rows),
+                        slice_rsrc(vbase + (int64_t)page * a.v_sb, sr.v_row_bytes, page_rows), in_page * sr.k_row_bytes,
+                        in_page * sr.v_row_bytes};
     }
-    return t;
+    return TileAddr{sr.k, sr.v, kv0 * sr.k_row_bytes, kv0 * sr.v_row_bytes};
 }
 
 template <typename T, int D>
@@ -864,7 +867,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // plus an immediate.  Per tile: wait for this wave's part of the tile, barrier
 // (publishes the tile and frees the buffer computed last), refill that buffer
 // with the tile STAGES - 1 ahead, compute.
-template <int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES, bool PAGED>
+template <int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES, int KVL>
 __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* __restrict__ kbase,
                                                 const __bf16* __restrict__ vbase, const QRegs<__bf16, D>& qr,
                                                 const int* __restrict__ part_idx, int n_part,
@@ -910,7 +913,7 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
     // K and V instructions per wave and tile (wave 0 adds one doc-id load).
     constexpr int kPerTile = 2 * DmaPlan<D>::kInsts;
     auto issue = [&](char* buf, int kv0) {
-        const TileAddr ta = tile_addr<__bf16, PAGED>(a, sr, kbase, vbase, b, kv0, S);
+        const TileAddr ta = tile_addr<__bf16, KVL>(a, sr, kbase, vbase, b, kv0, S);
 #pragma unroll
         for (int i = 0; i < DmaPlan<D>::kInsts; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ta.k, (lds_void_t*)(buf + (i * 4 + wave) * 1024), 16, pl.k[i],
@@ -989,7 +992,7 @@ __device__ __forceinline__ void attend_rows_dma(const FwdArgs& a, const __bf16* 
 // Walk tiles [tile_lo, tile_hi) of one row block's lists: partial tiles (masked)
 // first, then full tiles.  All waves load; active waves compute either key half
 // kh of every tile (KSPLIT) or both halves.
-template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES = 2, bool PAGED = false>
+template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int STAGES = 2, int KVL = kKvContig>
 __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restrict__ kbase, const T* __restrict__ vbase,
                                             const QRegs<T, D>& qr, const int* __restrict__ part_idx, int n_part,
                                             const int* __restrict__ full_idx, int tile_lo, int tile_hi,
@@ -997,7 +1000,7 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
                                             f32x16_t (&o)[D / 32], RowState<Precise<T>::value>& st, char* lds, int S,
                                             int b, int rot = 0) {
     if constexpr (sizeof(T) == 2) {
-        attend_rows_dma<D, SCORE, FIXED, KSPLIT, EXT, STAGES, PAGED>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
+        attend_rows_dma<D, SCORE, FIXED, KSPLIT, EXT, STAGES, KVL>(a, kbase, vbase, qr, part_idx, n_part, full_idx, tile_lo,
                                                          tile_hi, tc, row, wave_active, kh, o, st, lds, S, b, rot);
     } else {
     using G = Tiles<T, D>;
@@ -1027,7 +1030,7 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
     Stage<T, D> stage;
     bool masked;
     int kv0 = tile_kv0(tile_lo, masked);
-    stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, kv0, S), sr, kv0, with_doc, tid);
+    stage_load<T, D>(stage, so, tile_addr<T, KVL>(a, sr, kbase, vbase, b, kv0, S), sr, kv0, with_doc, tid);
     stage_store<T, D>(stage, lds, with_doc, tid);
     __syncthreads();
     for (int t = tile_lo; t < tile_hi; ++t) {
@@ -1037,7 +1040,7 @@ __device__ __forceinline__ void attend_rows(const FwdArgs& a, const T* __restric
         const bool has_next = t + 1 < tile_hi;
         if (has_next) {
             next_kv0 = tile_kv0(t + 1, next_masked);
-            stage_load<T, D>(stage, so, tile_addr<T, PAGED>(a, sr, kbase, vbase, b, next_kv0, S), sr, next_kv0, with_doc,
+            stage_load<T, D>(stage, so, tile_addr<T, KVL>(a, sr, kbase, vbase, b, next_kv0, S), sr, next_kv0, with_doc,
                              tid);
         }
         const char* cur = lds + buf * G::kBufBytes;
@@ -1141,10 +1144,10 @@ struct BatchView {
     int S;
 };
 
-template <bool PAGED>
+template <int KVL>
 __device__ __forceinline__ BatchView batch_view(const FwdArgs& a, int b) {
     BatchView v{a.mask.q_offset, a.S};
-    if constexpr (PAGED) {
+    if constexpr (KVL != kKvContig) {
         if (a.mask.q_offsets != nullptr)
             v.q_offset = min(max(scalar_load(a.mask.q_offsets + b), -(1 << 30)), 1 << 30);
         if (a.mask.kv_lens != nullptr) v.S = min(max(scalar_load(a.mask.kv_lens + b), 0), a.S);
@@ -1152,10 +1155,10 @@ __device__ __forceinline__ BatchView batch_view(const FwdArgs& a, int b) {
     return v;
 }
 
-template <typename T, bool PAGED>
+template <typename T, int KVL>
 __device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, int64_t sh, const FwdArgs& a, int b,
                                                  int hkv) {
-    const int64_t off = (PAGED && a.page_table != nullptr) ? (int64_t)hkv * sh : (int64_t)b * sb + (int64_t)hkv * sh;
+    const int64_t off = KVL == kKvPaged ? (int64_t)hkv * sh : (int64_t)b * sb + (int64_t)hkv * sh;
     return reinterpret_cast<const T*>(base) + off;
 }
 
@@ -1164,11 +1167,11 @@ __device__ __forceinline__ const T* kv_head_base(const void* base, int64_t sb, i
 // waves hide MFMA and LDS latency behind each other's VALU work), otherwise
 // as many as the registers of the wider tiles allow.  The extended kernels
 // (mask programs, max_scores) at head dim 64 need more than the 168 registers
-// of three waves and would spill, so they take two; the key-split paged ones
-// need more than the 128 of four and take three.
-template <typename T, int D, bool KSPLIT, bool EXT, bool PAGED = false> struct PrefillOccupancy {
+// of three waves and would spill, so they take two; the key-split paged and
+// per-batch ones need more than the 128 of four and take three.
+template <typename T, int D, bool KSPLIT, bool EXT, int KVL = kKvContig> struct PrefillOccupancy {
     static constexpr int value =
-        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 2 : (PAGED ? 3 : 4)) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
+        sizeof(T) == 2 ? (D == 64 ? (KSPLIT ? (EXT ? 2 : (KVL != kKvContig ? 3 : 4)) : (EXT ? 2 : 3)) : 2) : (D == 64 ? 2 : 1);
 };
 
 
@@ -1226,8 +1229,8 @@ static_assert(kLongestFirstMaxBlocks <= kThreads, "one Q block per thread when o
 // rows) and key half w >> 1 of every tile, which halves the tile loop of a
 // workgroup (short critical path when a few Q blocks hold most of the work);
 // otherwise a part is 128 rows, one 32-row group per wave, both key halves.
-template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, bool PAGED>
-__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT, PAGED>::value)) void attn_fwd_prefill(FwdArgs a) {
+template <typename T, int D, int SCORE, bool FIXED, bool KSPLIT, bool EXT, int KVL>
+__global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT, KVL>::value)) void attn_fwd_prefill(FwdArgs a) {
     using G = Tiles<T, D>;
     __shared__ __attribute__((aligned(16))) char lds[2 * G::kBufBytes];
     constexpr int kRows = KSPLIT ? 64 : 128;
@@ -1254,15 +1257,15 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT, PAGE
     LaneRow row;
     row.q_row = qb * a.q_block + r_in_blk;
     row.ok = r_in_blk < a.q_block && row.q_row < a.L;
-    const BatchView bv = batch_view<PAGED>(a, b);
+    const BatchView bv = batch_view<KVL>(a, b);
     row.q_pos = row.q_row + bv.q_offset;
     row.hq = hq;
     row.doc_q = lane_doc(a.mask, row.q_pos);
     const bool wave_active = part * kRows + rg * 32 < a.q_block;
 
     const T* qbase = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
-    const T* kbase = kv_head_base<T, PAGED>(a.k, a.k_sb, a.k_sh, a, b, hkv);
-    const T* vbase = kv_head_base<T, PAGED>(a.v, a.v_sb, a.v_sh, a, b, hkv);
+    const T* kbase = kv_head_base<T, KVL>(a.k, a.k_sb, a.k_sh, a, b, hkv);
+    const T* vbase = kv_head_base<T, KVL>(a.v, a.v_sb, a.v_sh, a, b, hkv);
 
     QRegs<T, D> qr;
     load_q<T, D>(qr, qbase + (int64_t)row.q_row * a.q_sr, row.ok, hf);
@@ -1278,7 +1281,7 @@ __global__ __launch_bounds__(kThreads, (PrefillOccupancy<T, D, KSPLIT, EXT, PAGE
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     RowState<Precise<T>::value> st{kNegInf, 0.0f, 0.0f, kNegInf};
-    attend_rows<T, D, SCORE, FIXED, KSPLIT, EXT, 2, PAGED>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB, n_part,
+    attend_rows<T, D, SCORE, FIXED, KSPLIT, EXT, 2, KVL>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB, n_part,
                                             a.full_idx + row_id * a.nKB, 0, n_tiles, tc, row, wave_active, kh, o, st,
                                             lds, bv.S, b);
     if constexpr (KSPLIT) merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
@@ -1332,7 +1335,7 @@ template <int D> struct DecodeShape {
 // divided into `splits` contiguous ranges; each workgroup writes its partial
 // numerator, base-2 reference and denominator.  bf16 only; the block mask must
 // be the same for every head (H = 1).
-template <int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
+template <int D, int SCORE, bool FIXED, bool EXT, int KVL>
 __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_fwd_decode(FwdArgs a) {
     using T = __bf16;
     using G = Tiles<T, D>;
@@ -1352,15 +1355,15 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
     row.q_row = qb * a.q_block + r % a.q_block;
     row.hq = hkv * a.group + g;
     row.ok = r < rows && row.q_row < a.L;
-    const BatchView bv = batch_view<PAGED>(a, b);
+    const BatchView bv = batch_view<KVL>(a, b);
     row.q_pos = row.q_row + bv.q_offset;
     row.doc_q = lane_doc(a.mask, row.q_pos);
     const bool wave_active = rg * 32 < rows;
 
     const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * a.q_sb + (int64_t)row.hq * a.q_sh +
                     (int64_t)row.q_row * a.q_sr;
-    const T* kbase = kv_head_base<T, PAGED>(a.k, a.k_sb, a.k_sh, a, b, hkv);
-    const T* vbase = kv_head_base<T, PAGED>(a.v, a.v_sb, a.v_sh, a, b, hkv);
+    const T* kbase = kv_head_base<T, KVL>(a.k, a.k_sb, a.k_sh, a, b, hkv);
+    const T* vbase = kv_head_base<T, KVL>(a.v, a.v_sb, a.v_sh, a, b, hkv);
     QRegs<T, D> qr;
     load_q<T, D>(qr, qrow, row.ok, hf);
 
@@ -1382,7 +1385,7 @@ __global__ __launch_bounds__(kThreads, DecodeShape<D>::kWavesPerSimd) void attn_
     // range apart at the same moment
     const int n_rng = t_hi - t_lo;
     const int rot = n_rng > 1 ? (int)(((uint32_t)blockIdx.x * 2654435761u >> 12) % (uint32_t)n_rng) : 0;
-    attend_rows<T, D, SCORE, FIXED, true, EXT, DecodeShape<D>::kStages, PAGED>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
+    attend_rows<T, D, SCORE, FIXED, true, EXT, DecodeShape<D>::kStages, KVL>(a, kbase, vbase, qr, a.kv_idx + row_id * a.nKB,
                                                                    n_part, a.full_idx + row_id * a.nKB, t_lo, t_hi,
                                                                    tc, row, wave_active, kh, o, st, lds, bv.S, b, rot);
     merge_key_halves<T, D, FIXED>(o, st, lds, rg, kh, lane, wave_active);
@@ -1448,30 +1451,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_combine(FwdArgs a) {
         a.lse[row] = live ? (float)(((double)ref_max + (double)__log2f(l)) * 0.6931471805599453) : kNegInf;
 }
 
-template <typename T, int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
+template <typename T, int D, int SCORE, bool FIXED, bool EXT, int KVL>
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const int rows = a.ksplit ? 64 : 128;
     const int64_t blocks = (int64_t)a.nQB * ((a.q_block + rows - 1) / rows) * a.B * a.Hq;
     if constexpr (D == 64 && sizeof(T) == 4) {
         // fp32 at head dim 64 always uses key-split workgroups (prefill_ksplit)
         if (!a.ksplit) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
+        hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, KVL>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, a);
     } else {
         if (a.ksplit)
-            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, PAGED>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, true, EXT, KVL>), dim3((unsigned)blocks),
                                dim3(kThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, false, EXT, PAGED>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((attn_fwd_prefill<T, D, SCORE, FIXED, false, EXT, KVL>), dim3((unsigned)blocks),
                                dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
 
-template <int D, int SCORE, bool FIXED, bool EXT, bool PAGED>
+template <int D, int SCORE, bool FIXED, bool EXT, int KVL>
 hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.B * a.Hkv * a.nQB * a.splits;
-    hipLaunchKernelGGL((attn_fwd_decode<D, SCORE, FIXED, EXT, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_decode<D, SCORE, FIXED, EXT, KVL>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)a.B * a.Hq * a.L;
@@ -1480,33 +1483,33 @@ hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DECODE, bool EXT, bool PAGED>
+template <typename T, int D, bool DECODE, bool EXT, int KVL>
 hipError_t dispatch_ext(const FwdArgs& a, hipStream_t stream) {
     const bool fixed = a.ref_mode == 1;
     if constexpr (DECODE) {
         switch (a.score_kind) {
-        case SCORE_NONE: return launch_decode<D, SCORE_NONE, false, EXT, PAGED>(a, stream);
+        case SCORE_NONE: return launch_decode<D, SCORE_NONE, false, EXT, KVL>(a, stream);
         case SCORE_SOFTCAP:
-            return fixed ? launch_decode<D, SCORE_SOFTCAP, true, EXT, PAGED>(a, stream)
-                         : launch_decode<D, SCORE_SOFTCAP, false, EXT, PAGED>(a, stream);
+            return fixed ? launch_decode<D, SCORE_SOFTCAP, true, EXT, KVL>(a, stream)
+                         : launch_decode<D, SCORE_SOFTCAP, false, EXT, KVL>(a, stream);
         case SCORE_SOFTCAP_ALIBI:
-            return fixed ? launch_decode<D, SCORE_SOFTCAP_ALIBI, true, EXT, PAGED>(a, stream)
-                         : launch_decode<D, SCORE_SOFTCAP_ALIBI, false, EXT, PAGED>(a, stream);
-        case SCORE_ALIBI: return launch_decode<D, SCORE_ALIBI, false, EXT, PAGED>(a, stream);
+            return fixed ? launch_decode<D, SCORE_SOFTCAP_ALIBI, true, EXT, KVL>(a, stream)
+                         : launch_decode<D, SCORE_SOFTCAP_ALIBI, false, EXT, KVL>(a, stream);
+        case SCORE_ALIBI: return launch_decode<D, SCORE_ALIBI, false, EXT, KVL>(a, stream);
         default: return hipErrorInvalidValue;
         }
     } else {
         switch (a.score_kind) {
-        case SCORE_NONE: return launch_prefill<T, D, SCORE_NONE, false, EXT, PAGED>(a, stream);
+        case SCORE_NONE: return launch_prefill<T, D, SCORE_NONE, false, EXT, KVL>(a, stream);
         case SCORE_SOFTCAP:
             if constexpr (sizeof(T) == 2)
-                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP, true, EXT, PAGED>(a, stream);
-            return launch_prefill<T, D, SCORE_SOFTCAP, false, EXT, PAGED>(a, stream);
+                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP, true, EXT, KVL>(a, stream);
+            return launch_prefill<T, D, SCORE_SOFTCAP, false, EXT, KVL>(a, stream);
         case SCORE_SOFTCAP_ALIBI:
             if constexpr (sizeof(T) == 2)
-                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, true, EXT, PAGED>(a, stream);
-            return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, false, EXT, PAGED>(a, stream);
-        case SCORE_ALIBI: return launch_prefill<T, D, SCORE_ALIBI, false, EXT, PAGED>(a, stream);
+                if (fixed) return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, true, EXT, KVL>(a, stream);
+            return launch_prefill<T, D, SCORE_SOFTCAP_ALIBI, false, EXT, KVL>(a, stream);
+        case SCORE_ALIBI: return launch_prefill<T, D, SCORE_ALIBI, false, EXT, KVL>(a, stream);
         default: return hipErrorInvalidValue;
         }
     }
@@ -1514,16 +1517,20 @@ hipError_t dispatch_ext(const FwdArgs& a, hipStream_t stream) {
 
 // Program masks and the max_scores output run in separately compiled
 // "extended" kernels, so the common kernels keep their register budget.
-// Paged caches and per-batch offsets and lengths (tiles remapped through the
-// page table, per-batch values read per workgroup) have their own kernels,
-// lean or extended by the same rule.
+// Paged pools (tiles remapped through the page table) and contiguous caches
+// with per-batch offsets and lengths (per-batch values read per workgroup)
+// have kernels of their own, lean or extended by the same rule.
 template <typename T, int D, bool DECODE>
 hipError_t dispatch(const FwdArgs& a, hipStream_t stream) {
     const bool ext = a.mask.kind == MASK_PROGRAM || a.max_scores != nullptr;
-    if (a.page_table != nullptr || a.mask.q_offsets != nullptr || a.mask.kv_lens != nullptr)
-        return ext ? dispatch_ext<T, D, DECODE, true, true>(a, stream) : dispatch_ext<T, D, DECODE, false, true>(a, stream);
-    if (ext) return dispatch_ext<T, D, DECODE, true, false>(a, stream);
-    return dispatch_ext<T, D, DECODE, false, false>(a, stream);
+    if (a.page_table != nullptr)
+        return ext ? dispatch_ext<T, D, DECODE, true, kKvPaged>(a, stream)
+                   : dispatch_ext<T, D, DECODE, false, kKvPaged>(a, stream);
+    if (a.mask.q_offsets != nullptr || a.mask.kv_lens != nullptr)
+        return ext ? dispatch_ext<T, D, DECODE, true, kKvPerBatch>(a, stream)
+                   : dispatch_ext<T, D, DECODE, false, kKvPerBatch>(a, stream);
+    if (ext) return dispatch_ext<T, D, DECODE, true, kKvContig>(a, stream);
+    return dispatch_ext<T, D, DECODE, false, kKvContig>(a, stream);
 }
 
 }  // namespace
