@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import programmable_block_sparse_amd as pbs
-from gpu_common import assert_attention_close, assert_block_mask_equal, require_gpu
+from gpu_common import TOL_LSE, assert_attention_close, assert_block_mask_equal, require_gpu
 from oracle import MaskMod, ScoreMod, attention, build_block_mask
 from oracle import default_scale as oracle_default_scale
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
@@ -34,13 +34,14 @@ def _i32(x, dev):
 
 
 def run(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, kind, window=0, sinks=0, offs, lens,
-        page_size=0, ring_pages=0, what=""):
+        page_size=0, ring_pages=0, clauses=(), with_max=False, what=""):
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, L, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
-    spec = pbs.MaskSpec(kind, window=window, sinks=sinks, q_offset=0, q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev))
-    mod = MaskMod(kind, window=window, sinks=sinks)
+    spec = pbs.MaskSpec(kind, window=window, sinks=sinks, q_offset=0, q_offsets=_i32(offs, dev), kv_lens=_i32(lens, dev),
+                        clauses=clauses)
+    mod = MaskMod(kind, window=window, sinks=sinks, clauses=clauses)
     bm = pbs.flex_blockmask_build(spec, L, S, qb, kb, B=B, device=dev)
     assert_block_mask_equal(bm, build_block_mask(mod, L, S, qb, kb, B=B, q_offset=offs, kv_len=lens))
     sspec, smod = pbs.ScoreSpec(**score), ScoreMod(**score)
@@ -66,16 +67,27 @@ def run(dev, *, seed, dtype, B, Hq, Hkv, L, S, D, qb, kb, score, kind, window=0,
             for p in range(-(-lens[b] // page_size)):
                 pool_k[table[b, p]] = kp[b, :, p * page_size:(p + 1) * page_size]
                 pool_v[table[b, p]] = vp[b, :, p * page_size:(p + 1) * page_size]
-        out, lse, _ = pbs.flex_attn_fwd_paged(qt, _t(pool_k, dtype, dev), _t(pool_v, dtype, dev),
-                                              torch.from_numpy(table).to(dev), S=S, block_mask=bm, score=sspec,
-                                              mask=spec)
+        out, lse, mx = pbs.flex_attn_fwd_paged(qt, _t(pool_k, dtype, dev), _t(pool_v, dtype, dev),
+                                               torch.from_numpy(table).to(dev), S=S, block_mask=bm, score=sspec,
+                                               mask=spec, return_max_scores=with_max)
+    elif with_max:
+        out, lse, mx = pbs.flex_attn_fwd_aux(qt, _t(k, dtype, dev), _t(v, dtype, dev), block_mask=bm, score=sspec,
+                                             mask=spec)
     else:
         out, lse = pbs.flex_attn_fwd(qt, _t(k, dtype, dev), _t(v, dtype, dev), block_mask=bm, score=sspec, mask=spec)
     torch.cuda.synchronize()
     sc = oracle_default_scale(D)
-    out_ref, lse_ref = attention(_w(q, dtype), _w(k, dtype), _w(v, dtype), scale=sc, score=smod, mask=mod,
-                                 q_offset=offs, kv_len=lens)
+    out_ref, lse_ref, mx_ref = attention(_w(q, dtype), _w(k, dtype), _w(v, dtype), scale=sc, score=smod, mask=mod,
+                                         q_offset=offs, kv_len=lens, with_max=True)
     assert_attention_close(out, lse, out_ref, lse_ref, dtype, what)
+    if with_max:
+        # the row maximum is a score like lse: same error sources, same bound
+        m = mx.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isneginf(m), np.isneginf(mx_ref)), f"{what}: -inf pattern of max_scores"
+        fin = ~np.isneginf(mx_ref)
+        merr = np.abs(m[fin] - mx_ref[fin]).max() if fin.any() else 0.0
+        print(f"[decode] {what}: max_scores max-abs {merr:.3e}")
+        assert merr <= TOL_LSE, f"{what}: max_scores max-abs {merr:.3e}"
 
 
 def test_per_batch_offsets_and_lengths_prefill(dev):
@@ -114,6 +126,30 @@ def test_paged_cache_128_row_workgroups(dev):
     run(dev, seed=31, dtype="bf16", B=3, Hq=128, Hkv=32, L=200, S=700, D=64, qb=128, kb=64,
         score=dict(kind="softcap_alibi", cap=30.0), kind="causal", offs=[500, 120, 0], lens=[700, 320, 200],
         page_size=128, what="paged bf16 D=64 128-row workgroups")
+
+
+def test_per_batch_128_row_workgroups(dev):
+    """The contiguous counterpart of the paged case above: per-batch offsets
+    and lengths over contiguous caches in 128-row workgroups."""
+    run(dev, seed=32, dtype="bf16", B=3, Hq=128, Hkv=32, L=200, S=700, D=64, qb=128, kb=64,
+        score=dict(kind="softcap_alibi", cap=30.0), kind="causal", offs=[500, 120, 0], lens=[700, 320, 200],
+        what="per-batch bf16 D=64 128-row workgroups")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_extended_kernels_per_batch(dev, paged, dtype, D):
+    """Mask programs and the row maxima with per-batch offsets and lengths,
+    contiguous and paged: the extended kernels of both cache layouts."""
+    clauses = (("causal", 0),), (("window", 90), ("kv_lt", 8))
+    run(dev, seed=40 + D, dtype=dtype, B=3, Hq=4, Hkv=2, L=150, S=520, D=D, qb=64, kb=64,
+        score=dict(kind="softcap", cap=20.0), kind="program", clauses=clauses, offs=[370, 0, 60],
+        lens=[520, 140, 250], page_size=128 if paged else 0, with_max=True,
+        what=f"program per batch {dtype} D={D} paged={paged}")
+    # 16-query verify steps under GQA with the row maxima: the extended decode kernel
+    run(dev, seed=50 + D, dtype=dtype, B=2, Hq=8, Hkv=2, L=16, S=1200, D=D, qb=16, kb=64,
+        score=dict(kind="softcap", cap=50.0), kind="causal", offs=[1184, 400], lens=[1200, 416],
+        page_size=64 if paged else 0, with_max=True, what=f"decode max_scores {dtype} D={D} paged={paged}")
 
 
 def test_circular_buffer(dev):
