@@ -519,6 +519,39 @@ def test_attention_program_masks(dev, dtype, D):
                  what=f"{dtype} D={D} {name} {score}")
 
 
+def test_attention_fuzz_small(dev):
+    """Random small cases over the whole menu: ragged L and S (L > S too),
+    offsets, tile shapes, GQA ratios, head dims, dtypes, every mask kind (with
+    random windows, sinks, documents and programs) and every score kind."""
+    rng = np.random.default_rng(2468)
+    kinds = ["noop", "causal", "causal_window_sinks", "doc_causal", "program"]
+    scores = [dict(kind="none"), dict(kind="alibi", alibi_m=8.0)] + \
+        [dict(kind=k, cap=float(c)) for k in ("softcap", "softcap_alibi") for c in (3.0, 20.0, 50.0)]
+    for trial in range(40):
+        dtype = "bf16" if trial % 3 else "f32"
+        D = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.integers(1, 3))
+        L, S = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        qb = int(rng.choice([16, 32, 64, 128]))
+        kb = int(rng.choice([64, 128]))
+        kind = kinds[trial % len(kinds)]
+        score = scores[int(rng.integers(0, len(scores)))]
+        off = None if trial % 4 else int(rng.integers(-40, 60))
+        clauses = _random_program(rng, True, True) if kind == "program" else ()
+        eff = S - L if off is None else off
+        if eff < 0 and _uses_doc(kind, clauses):
+            off = -eff   # document masks take q_offset >= 0 (a documented argument check)
+        bm_heads = Hkv * G if any(n == "head_lt" for c in clauses for n, _ in c) else 1
+        window, sinks = (int(rng.integers(1, 120)), int(rng.integers(0, 8))) if kind == "causal_window_sinks" else (0, 0)
+        what = (f"fuzz {trial}: {dtype} D={D} G={G} Hkv={Hkv} L={L} S={S} tiles {qb}x{kb} {kind} {score} "
+                f"off={off} w={window} s={sinks} {clauses}")
+        print(f"[parity] {what}", flush=True)
+        run_case(dev, seed=3000 + trial, dtype=dtype, B=2, Hq=Hkv * G, Hkv=Hkv, L=L, S=S, D=D, qb=qb, kb=kb,
+                 score=score, mask_kind=kind, window=window, sinks=sinks, q_offset=off, clauses=clauses,
+                 bm_heads=bm_heads, what=what)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_softcap_alibi_programs_that_hide_the_diagonal(dev, D):
     """Soft-cap plus distance bias under mask programs with a causal clause
