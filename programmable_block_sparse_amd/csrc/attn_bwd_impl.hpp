@@ -467,6 +467,10 @@ __device__ __forceinline__ int bwd_key_splits(const BwdArgs& a, int b, int hkv, 
     return min(max((n + a.chunk_tiles - 1) / a.chunk_tiles, 1), a.kv_splits);
 }
 
+// Most workgroups that share one 64-key column (the host's bwd_kv_splits
+// caps the split count at this; launch_bwd_passes rejects more).
+constexpr int kBwdMaxSplits = 4;
+
 // fp32 partial sums of split `split` of 64-key column `col` (bh * per_bh + kt):
 // 64 x D for dk, then 64 x D for dv.
 __device__ __forceinline__ float* bwd_partial(const BwdArgs& a, int split, int col, int D) {
@@ -746,20 +750,45 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_reduce(BwdArgs a) {
     const int nch = bwd_key_splits(a, b, hkv, kt / subs);
     if (nch == 1) return;
     const int kv0 = kt * kTileN;
-    for (int e = threadIdx.x * 4; e < 64 * D; e += kThreads * 4) {
-        const int key = kv0 + e / D, d = e % D;
-        if (key >= a.S) break;
-        float4 sk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sv = sk;
-        for (int sp = 0; sp < nch; ++sp) {
-            const float* part = bwd_partial(a, sp, col, D);
-            const float4 k4 = *reinterpret_cast<const float4*>(part + e);
-            const float4 v4 = *reinterpret_cast<const float4*>(part + 64 * D + e);
-            sk.x += k4.x; sk.y += k4.y; sk.z += k4.z; sk.w += k4.w;
-            sv.x += v4.x; sv.y += v4.y; sv.z += v4.z; sv.w += v4.w;
+    // Each thread owns kPer float4 positions of the column.  Every partial of
+    // two positions is loaded before any is added, so a thread waits on memory
+    // once per pair of positions instead of once per load; the sums still run
+    // in split order.  Positions past S are loaded (the partial arrays cover
+    // all 64 keys of a column) but not stored.
+    constexpr int kPer = 64 * D / (kThreads * 4);
+    static_assert(kPer % 2 == 0, "positions go in pairs");
+#pragma unroll 1
+    for (int i0 = 0; i0 < kPer; i0 += 2) {
+        float4 pk[2][kBwdMaxSplits], pv[2][kBwdMaxSplits];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = (threadIdx.x + (i0 + i) * kThreads) * 4;
+#pragma unroll
+            for (int sp = 0; sp < kBwdMaxSplits; ++sp) {
+                if (sp < nch) {
+                    const float* part = bwd_partial(a, sp, col, D);
+                    pk[i][sp] = *reinterpret_cast<const float4*>(part + e);
+                    pv[i][sp] = *reinterpret_cast<const float4*>(part + 64 * D + e);
+                }
+            }
         }
-        const int64_t o = ((int64_t)bh * a.S + key) * D + d;
-        store_out4<T>(reinterpret_cast<T*>(a.dk) + o, sk.x, sk.y, sk.z, sk.w);
-        store_out4<T>(reinterpret_cast<T*>(a.dv) + o, sv.x, sv.y, sv.z, sv.w);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = (threadIdx.x + (i0 + i) * kThreads) * 4;
+            const int key = kv0 + e / D, d = e % D;
+            if (key >= a.S) continue;
+            float4 sk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), sv = sk;
+#pragma unroll
+            for (int sp = 0; sp < kBwdMaxSplits; ++sp) {
+                if (sp < nch) {
+                    sk.x += pk[i][sp].x; sk.y += pk[i][sp].y; sk.z += pk[i][sp].z; sk.w += pk[i][sp].w;
+                    sv.x += pv[i][sp].x; sv.y += pv[i][sp].y; sv.z += pv[i][sp].z; sv.w += pv[i][sp].w;
+                }
+            }
+            const int64_t o = ((int64_t)bh * a.S + key) * D + d;
+            store_out4<T>(reinterpret_cast<T*>(a.dk) + o, sk.x, sk.y, sk.z, sk.w);
+            store_out4<T>(reinterpret_cast<T*>(a.dv) + o, sv.x, sv.y, sv.z, sv.w);
+        }
     }
 }
 
@@ -955,6 +984,7 @@ template <typename T, int D, int SCORE, bool EXT>
 hipError_t launch_bwd_passes(const BwdArgs& a, hipStream_t stream) {
     const int64_t kv_items = (int64_t)a.B * a.Hkv * a.nKB * (a.kv_block / kTileN);
     const int64_t q_items = (int64_t)a.B * a.Hq * a.nQB * (a.q_block / 64);
+    if (a.kv_splits > kBwdMaxSplits) return hipErrorInvalidValue;   // the reduce sums at most that many
     hipError_t e;
     // one launch for GQA at head dim 128 (bf16, element-rule masks); two
     // otherwise: at head dim 64 the query-major pass alone runs at a higher
