@@ -513,6 +513,11 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, char* lds, lds_char_
     const int q_off = batch_q_offset(a.mask, b), S_b = batch_kv_len(a.mask, b, a.S);
     const int kvb = kt / subs;
     const int kv0 = kt * kTileN;
+    // Splits past the ones this column needs have no work: leave before the
+    // K/V rows are loaded (and, at head dim 128, partly spilled to scratch).
+    // Only split launches have such workgroups; without splits the count is
+    // taken below, after the loads are issued.
+    if (a.kv_splits > 1 && split >= bwd_key_splits(a, b, hkv, kvb)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), hf = lane >> 5;
     const int kh = wave & 1, qh = wave >> 1;
     const int key = kv0 + 32 * kh + (lane & 31);
